@@ -1,0 +1,280 @@
+"""Thin ctypes binding of libcsa2.so: the same six calls and helpers as
+``include/csa2.h``.
+
+Marshalling only: each function checks tensor device/dtype/contiguity, derives
+sizes from shapes, allocates missing outputs/workspaces with torch (device
+memory only) and calls the C entry point on the current (or given) stream.
+Every step of the layer runs in the library's HIP kernels.  If the library has
+not been built this module raises at first use; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+_c_p, _c_i, _c_ll, _c_f, _c_d, _c_sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong,
+                                       ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+
+_SIGS = {
+    "csa2_version": ([], ctypes.c_char_p),
+    "csa2_status_string": ([_c_i], ctypes.c_char_p),
+    "csa2_last_error": ([], ctypes.c_char_p),
+    "csa2_compress": ([_c_p, _c_i, _c_i, _c_i, _c_i, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_ll,
+                       _c_i, _c_d, _c_p, _c_p], _c_i),
+    "csa2_quant_fp4": ([_c_p, _c_ll, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_p], _c_i),
+    "csa2_index_full_workspace": ([_c_i, _c_i, _c_i, _c_i, _c_i, _c_i], _c_sz),
+    "csa2_index_full": ([_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_p, _c_i, _c_p, _c_p,
+                         _c_p, _c_i, _c_i, _c_i, _c_p, _c_sz, _c_p], _c_i),
+    "csa2_topk_workspace": ([_c_i, _c_i, _c_i], _c_sz),
+    "csa2_topk": ([_c_p, _c_i, _c_i, _c_p, _c_p, _c_i, _c_p, _c_p, _c_sz, _c_p], _c_i),
+    "csa2_index_reindex_workspace": ([_c_i, _c_i, _c_i], _c_sz),
+    "csa2_index_reindex": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_i, _c_p,
+                            _c_p, _c_sz, _c_p], _c_i),
+    "csa2_sparse_attn_workspace": ([_c_i, _c_i, _c_i, _c_i, _c_i, _c_i], _c_sz),
+    "csa2_sparse_attn": ([_c_p, _c_p, _c_p, _c_i, _c_p, _c_i, _c_p, _c_f, _c_i, _c_ll, _c_i, _c_p,
+                          _c_i, _c_i, _c_i, _c_i, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p], _c_i),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcsa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_compression_03_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+class CSA2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        L = lib()
+        super().__init__(f"{fn}: {L.csa2_status_string(status).decode()}: "
+                         f"{L.csa2_last_error().decode()}")
+        self.status = status
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise CSA2Error(name, st)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+U8 = (torch.uint8, torch.float8_e4m3fn)
+I32 = (torch.int32,)
+F32 = (torch.float32,)
+
+
+def _ws(nbytes: int, like: torch.Tensor, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
+    return ws
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ------------------------------------------------------------------ helpers
+
+def csa2_version() -> str:
+    return lib().csa2_version().decode()
+
+
+def csa2_index_full_workspace(B, Tq, N, G=128, PB=2048, PE=8) -> int:
+    return lib().csa2_index_full_workspace(B, Tq, N, G, PB, PE)
+
+
+def csa2_topk_workspace(R, N, K) -> int:
+    return lib().csa2_topk_workspace(R, N, K)
+
+
+def csa2_index_reindex_workspace(B, P, K) -> int:
+    return lib().csa2_index_reindex_workspace(B, P, K)
+
+
+def csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) -> int:
+    return lib().csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S)
+
+
+# ------------------------------------------------------------------ the six calls
+
+def csa2_compress(H, W_kv, W_z, m: int, pos0: int = 0, rope_dim: int = 64,
+                  rope_theta: float = 10000.0, out=None, stream=None) -> torch.Tensor:
+    """H [B, T, d_model] (f32 or bf16), W_kv [d_model, d], W_z [d_model, d or 1] -> [B, T//m, d] f32."""
+    _dev(H, "H", F32 + BF16)
+    _dev(W_kv, "W_kv", F32 + BF16)
+    _dev(W_z, "W_z", F32 + BF16)
+    B, T, dm = H.shape
+    d, dz = W_kv.shape[1], W_z.shape[1]
+    dt = DTYPE_F32 if H.dtype == torch.float32 else DTYPE_BF16
+    wdt = DTYPE_F32 if W_kv.dtype == torch.float32 else DTYPE_BF16
+    if out is None:
+        out = torch.empty(B, T // m, d, dtype=torch.float32, device=H.device)
+    _dev(out, "out", F32)
+    _call("csa2_compress", _p(H), dt, B, T, dm, _p(W_kv), _p(W_z), wdt, d, dz, m, pos0, rope_dim,
+          float(rope_theta), _p(out), _stream(stream))
+    return out
+
+
+def csa2_quant_fp4(kv, codes=None, scales=None, W_ik=None, k_idx=None, stream=None):
+    """kv [..., d] f32 -> (codes [..., d/2] u8, scales [..., d/16] u8[, k_idx [..., d_i] bf16])."""
+    _dev(kv, "kv", F32)
+    d = kv.shape[-1]
+    lead = kv.shape[:-1]
+    n = kv.numel() // d
+    if codes is None:
+        codes = torch.empty(*lead, d // 2, dtype=torch.uint8, device=kv.device)
+    if scales is None:
+        scales = torch.empty(*lead, d // 16, dtype=torch.uint8, device=kv.device)
+    _dev(codes, "codes", U8)
+    _dev(scales, "scales", U8)
+    d_i = 0
+    if W_ik is not None:
+        _dev(W_ik, "W_ik", BF16)
+        d_i = W_ik.shape[1]
+        if k_idx is None:
+            k_idx = torch.empty(*lead, d_i, dtype=torch.bfloat16, device=kv.device)
+        _dev(k_idx, "k_idx", BF16)
+    _call("csa2_quant_fp4", _p(kv), n, d, _p(codes), _p(scales), _p(W_ik), d_i, _p(k_idx),
+          _stream(stream))
+    return (codes, scales) if W_ik is None else (codes, scales, k_idx)
+
+
+def csa2_index_full(q_idx, w, k_idx, q_pos=None, m: int = 1, scores=None, pool=None, pool_len=None,
+                    G: int = 128, PB: int = 2048, PE: int = 8, with_pool: bool = False, ws=None,
+                    stream=None):
+    """q_idx [B, Tq, h_i, d_i] bf16, w [B, Tq, h_i] f32, k_idx [B, N, d_i] bf16 ->
+    scores [B, Tq, N] (and pool [B*Tq, PB*PE], pool_len [B*Tq] when with_pool)."""
+    _dev(q_idx, "q_idx", BF16)
+    _dev(w, "w", F32)
+    _dev(k_idx, "k_idx", BF16)
+    B, Tq, h_i, d_i = q_idx.shape
+    N = k_idx.shape[1]
+    if q_pos is not None:
+        _dev(q_pos, "q_pos", I32)
+    if scores is None:
+        scores = torch.empty(B, Tq, N, dtype=torch.float32, device=q_idx.device)
+    _dev(scores, "scores", F32)
+    nbytes = 0
+    if with_pool or pool is not None:
+        if pool is None:
+            pool = torch.empty(B * Tq, PB * PE, dtype=torch.int32, device=q_idx.device)
+        if pool_len is None:
+            pool_len = torch.empty(B * Tq, dtype=torch.int32, device=q_idx.device)
+        _dev(pool, "pool", I32)
+        _dev(pool_len, "pool_len", I32)
+        nbytes = csa2_index_full_workspace(B, Tq, N, G, PB, PE)
+        ws = _ws(nbytes, q_idx, ws)
+    _call("csa2_index_full", _p(q_idx), _p(w), _p(k_idx), B, Tq, N, h_i, d_i, _p(q_pos), m,
+          _p(scores), _p(pool), _p(pool_len), G, PB, PE, _p(ws), _nbytes(ws), _stream(stream))
+    return (scores, pool, pool_len) if pool is not None else scores
+
+
+def csa2_topk(scores, K: int, valid_len=None, cand_map=None, out=None, ws=None, stream=None):
+    """scores [R, N] f32 -> [R, K] int32 ascending indices, -1 padded."""
+    _dev(scores, "scores", F32)
+    N = scores.shape[-1]
+    R = scores.numel() // N if N else 0
+    if valid_len is not None:
+        _dev(valid_len, "valid_len", I32)
+    if cand_map is not None:
+        _dev(cand_map, "cand_map", I32)
+    if out is None:
+        out = torch.empty(R, K, dtype=torch.int32, device=scores.device)
+    _dev(out, "out", I32)
+    ws = _ws(csa2_topk_workspace(R, N, K), scores, ws)
+    _call("csa2_topk", _p(scores), R, N, _p(valid_len), _p(cand_map), K, _p(out), _p(ws),
+          _nbytes(ws), _stream(stream))
+    return out
+
+
+def csa2_index_reindex(q_idx, w, k_idx, pool, pool_len, K: int = 512, sel=None, ws=None,
+                       stream=None):
+    """q_idx [B, h_i, d_i], w [B, h_i], k_idx [B, N, d_i], pool [B, P], pool_len [B] -> sel [B, K]."""
+    _dev(q_idx, "q_idx", BF16)
+    _dev(w, "w", F32)
+    _dev(k_idx, "k_idx", BF16)
+    _dev(pool, "pool", I32)
+    _dev(pool_len, "pool_len", I32)
+    B, h_i, d_i = q_idx.shape[0], q_idx.shape[-2], q_idx.shape[-1]
+    N = k_idx.shape[1]
+    P = pool.shape[-1]
+    if sel is None:
+        sel = torch.empty(B, K, dtype=torch.int32, device=q_idx.device)
+    _dev(sel, "sel", I32)
+    ws = _ws(csa2_index_reindex_workspace(B, P, K), q_idx, ws)
+    _call("csa2_index_reindex", _p(q_idx), _p(w), _p(k_idx), _p(pool), _p(pool_len), B, P, N, h_i,
+          d_i, K, _p(sel), _p(ws), _nbytes(ws), _stream(stream))
+    return sel
+
+
+def csa2_sparse_attn(q, codes, scales, sel, swa, swa_scale: float = 1.0, q_pos=None,
+                     swa_pos0: int = 0, n_win: int = 128, sm_scale: float = 0.0, out=None, lse=None,
+                     ws=None, stream=None):
+    """q [B, Tq, H_q, d] bf16, codes [B, N, d/2], scales [B, N, d/16], sel [B, Tq, K],
+    swa [B, S, d] E4M3 -> out [B, Tq, H_q, d] f32."""
+    _dev(q, "q", BF16)
+    _dev(codes, "codes", U8)
+    _dev(scales, "scales", U8)
+    _dev(sel, "sel", I32)
+    _dev(swa, "swa", U8)
+    B, Tq, H_q, d = q.shape
+    N = codes.shape[1]
+    K = sel.shape[-1]
+    S = swa.shape[1]
+    if q_pos is not None:
+        _dev(q_pos, "q_pos", I32)
+    if out is None:
+        out = torch.empty(B, Tq, H_q, d, dtype=torch.float32, device=q.device)
+    _dev(out, "out", F32)
+    if lse is not None:
+        _dev(lse, "lse", F32)
+    ws = _ws(csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S), q, ws)
+    _call("csa2_sparse_attn", _p(q), _p(codes), _p(scales), N, _p(sel), K, _p(swa),
+          float(swa_scale), S, swa_pos0, n_win, _p(q_pos), B, Tq, H_q, d, float(sm_scale), _p(out),
+          _p(lse), _p(ws), _nbytes(ws), _stream(stream))
+    return out

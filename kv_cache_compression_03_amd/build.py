@@ -1,0 +1,69 @@
+"""Build libcsa2.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m kv_cache_compression_03_amd.build   (or build() from Python)
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OBJ = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libcsa2.so")
+
+SOURCES = ["api.cpp", "quant.hip", "compress.hip", "index.hip", "topk.hip", "attn.hip"]
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # fp32 division must be IEEE correctly rounded: the FP4 codes depend on it
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # no packed fp32 instructions anywhere
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in (r.stderr or "").splitlines()
+                     if "packed-fp32-ops" not in l)  # host pass does not know the feature
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
+    if errs.strip():
+        print(errs, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libcsa2.so; always rebuilds."""
+    os.makedirs(OBJ, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

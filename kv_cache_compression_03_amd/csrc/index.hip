@@ -1,0 +1,139 @@
+// Indexer scores: s_j = sum_h w_h * max(0, q_h · k_j)  (Full and Reindex modes).
+//
+// [deep-dive §3.1, §3.2] Indexer Q x Indexer K -> score -> Top-K; Reindex rescores
+// only the shared pool [deep-dive §3.3].  Reading: ReLU per head, weighted sum.
+//
+// The contraction per entry is [h_i x d_i]·[d_i], 16 bf16 flops per byte of key,
+// so a decode step is bound by streaming the keys from HBM.  One MFMA
+// 16x16x32 bf16 handles 16 entries: A = the query heads (16 rows: 16/h_i
+// queries of h_i heads, rows past Tq are zero), B = 16 keys.  Each wave keeps
+// its queries in registers for its whole entry range and streams keys straight
+// from global memory into the B operand.  The reduction axis is permuted so
+// that lane (entry e, slot group g) reads d_i*2/4 contiguous bytes of key e;
+// the queries are loaded with the same permutation, so the dot products are
+// unchanged.  The ReLU / head-weight / head-sum epilogue runs on the MFMA
+// output: a lane holds 4 heads of one query for one entry, and one or two
+// cross-lane adds finish the head sum.
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+
+constexpr int kScanWaves = 4;
+constexpr int kScanBatch = 4;  // entry tiles whose keys are in flight together
+
+template <int HI, int DI>
+__global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, const int* __restrict__ gather,
+    const int* __restrict__ gather_len, const int* __restrict__ q_pos, int m, int Tq, int N, int L,
+    int tiles_per_wave, float* __restrict__ scores) {
+  constexpr int QPT = 16 / HI;     // queries per A tile
+  constexpr int KS = DI / 32;      // MFMA reduction steps
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * QPT;
+
+  // ---- queries (A operand) and head weights, kept for the whole range
+  bf16x8_t qa[KS];
+  {
+    const int t = t0 + col / HI, h = col % HI;
+    const uint4* qrow = reinterpret_cast<const uint4*>(q_idx + (((size_t)b * Tq + t) * HI + h) * DI);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (t < Tq) v = qrow[g * KS + s];
+      qa[s] = as_bf16x8(v);
+    }
+  }
+  float wr[4];
+  int nvis_row = L;  // entries visible to this lane's query (decode: all)
+  const int myq = t0 + (4 * g) / HI;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i, t = t0 + r / HI;
+    wr[i] = t < Tq ? w[((size_t)b * Tq + t) * HI + (r % HI)] : 0.0f;
+  }
+  if (q_pos != nullptr && myq < Tq) {
+    long long p = q_pos[(size_t)b * Tq + myq];
+    long long nv = (p + 1) / m;
+    nvis_row = (int)(nv < 0 ? 0 : (nv > L ? L : nv));
+  }
+  int Lb = L;
+  if (gather_len != nullptr) Lb = min(L, gather_len[b]);
+
+  const long long wave_first = ((long long)blockIdx.x * kScanWaves + wave) * tiles_per_wave * 16;
+  const uint16_t* kb = k_idx + (size_t)b * N * DI;
+  const int* gb = gather ? gather + (size_t)b * L : nullptr;
+  const bool writer = (g % (HI / 4 >= 1 ? HI / 4 : 1)) == 0 && myq < Tq;
+  float* srow = scores + ((size_t)b * Tq + (myq < Tq ? myq : 0)) * L;
+
+  for (int tile = 0; tile < tiles_per_wave; tile += kScanBatch) {
+    uint4 kv[kScanBatch][KS];
+    int ent[kScanBatch];
+    bool ent_ok[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const long long e = wave_first + (long long)(tile + u) * 16 + col;
+      ent[u] = (int)e;
+      bool live = (tile + u) < tiles_per_wave && e < Lb;
+      long long row = e;
+      if (live && gb) {
+        row = gb[e];
+        live = row >= 0 && row < N;  // an entry outside the cache scores -inf
+      }
+      ent_ok[u] = live;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kv[u][s] = make_uint4(0, 0, 0, 0);
+      if (live) {
+        const uint4* kr = reinterpret_cast<const uint4*>(kb + (size_t)row * DI);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kv[u][s] = kr[g * KS + s];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      if (tile + u >= tiles_per_wave) break;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma16x16x32(qa[s], as_bf16x8(kv[u][s]), acc);
+      float v = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(wr[i], fmaxf(acc[i], 0.0f), v);
+      if (HI >= 8) v += __shfl_xor(v, 16);
+      if (HI >= 16) v += __shfl_xor(v, 32);
+      const int e = ent[u];
+      if (writer && e < L) srow[e] = (ent_ok[u] && e < nvis_row) ? v : -INFINITY;
+    }
+  }
+}
+
+hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                               const int* gather, const int* gather_len, const int* q_pos, int m,
+                               int B, int Tq, int N, int L, int h_i, int d_i, float* scores,
+                               hipStream_t st) {
+  if (B == 0 || Tq == 0 || L == 0) return hipSuccess;
+  const int qpt = 16 / h_i;
+  const int qgroups = (Tq + qpt - 1) / qpt;
+  const long long tiles = ((long long)L + 15) / 16;
+  // aim for >= 2048 workgroups in total, at most 32 tiles (512 entries) per wave
+  long long per_wave = ((long long)tiles * B * qgroups + 2048LL * kScanWaves - 1) / (2048LL * kScanWaves);
+  int tpw = (int)(per_wave < 1 ? 1 : (per_wave > 32 ? 32 : per_wave));
+  tpw = (tpw + kScanBatch - 1) / kScanBatch * kScanBatch;
+  const long long bx = (tiles + (long long)tpw * kScanWaves - 1) / ((long long)tpw * kScanWaves);
+  dim3 grid((unsigned)bx, (unsigned)qgroups, (unsigned)B), block(kScanWaves * 64);
+#define CSA2_SCAN(HI_, DI_)                                                                    \
+  hipLaunchKernelGGL((index_scores_kernel<HI_, DI_>), grid, block, 0, st, q_idx, w, k_idx, gather, \
+                     gather_len, q_pos, m, Tq, N, L, tpw, scores)
+  if (h_i == 8 && d_i == 128) CSA2_SCAN(8, 128);
+  else if (h_i == 8 && d_i == 64) CSA2_SCAN(8, 64);
+  else if (h_i == 4 && d_i == 128) CSA2_SCAN(4, 128);
+  else if (h_i == 4 && d_i == 64) CSA2_SCAN(4, 64);
+  else if (h_i == 16 && d_i == 128) CSA2_SCAN(16, 128);
+  else CSA2_SCAN(16, 64);
+#undef CSA2_SCAN
+  return hipGetLastError();
+}
+
+}  // namespace csa2

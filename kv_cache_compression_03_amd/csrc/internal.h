@@ -1,0 +1,60 @@
+// Launchers of the CSA2 kernels, called by the C ABI layer (api.cpp) after it has
+// validated every argument.  Each returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kTopkCap = 8192;  // candidates a Top-K row sorts in LDS
+
+// quant.hip
+hipError_t launch_quant_fp4(const float* kv, long long n, int d, uint8_t* codes, uint8_t* scales,
+                            hipStream_t st);
+hipError_t launch_indexer_k(const uint8_t* codes, const uint8_t* scales, long long n, int d,
+                            const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st);
+
+// compress.hip
+hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_model, const void* W_kv,
+                           const void* W_z, int d, int d_z, int m, long long pos0, int rope_dim,
+                           double rope_theta, float* kv_out, hipStream_t st);
+
+// index.hip: scores[b, t, i] for rows i < L of sequence b (rows gathered through
+// `gather` when not null).
+hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                               const int* gather, const int* gather_len, const int* q_pos, int m,
+                               int B, int Tq, int N, int L, int h_i, int d_i, float* scores,
+                               hipStream_t st);
+
+// topk.hip
+struct TopkWs {
+  float* cmax;      // [R, 2K]
+  int* cnt;         // [R]
+  float* cscore;    // [R, cap]
+  int* cidx;        // [R, cap]
+};
+size_t topk_ws_bytes(int R, int N, int K);
+TopkWs topk_ws_carve(void* ws, int R, int K);
+hipError_t launch_topk(const float* scores, int R, int N, const int* valid_len, const int* cand_map,
+                       int K, int* out_idx, const TopkWs& ws, hipStream_t st);
+
+// pool (topk.hip)
+size_t pool_ws_bytes(int R, int N, int G, int PB);
+hipError_t launch_pool(const float* scores, int R, int N, const int* q_pos, int m, int G, int PB,
+                       int PE, int* pool, int* pool_len, void* ws, hipStream_t st);
+
+// attn.hip
+struct AttnPlan {
+  int waves, head_groups, n_splits, chunks_per_split;
+};
+AttnPlan attn_plan(int B, int Tq, int H_q, int K, int S);
+size_t attn_ws_bytes(int B, int Tq, int H_q, int d, int K, int S);
+hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, int N,
+                              const int* sel, int K, const uint8_t* swa, float swa_scale, int S,
+                              long long swa_pos0, int n_win, const int* q_pos, int B, int Tq,
+                              int H_q, int d, float sm_scale, float* out, float* lse, void* ws,
+                              hipStream_t st);
+
+}  // namespace csa2

@@ -1,0 +1,125 @@
+// FP4 main-KV quantisation and the indexer-key projection.
+//
+// [daily 核心机制; deep-dive §3.4] main KV as E2M1 elements with one E4M3 scale
+// per 16 channels, quantised after RoPE; [deep-dive §3.1] the indexer K is a
+// projection of the main KV.  Readings: absmax scale s = E4M3(amax/6), codes
+// E2M1(x/s), both nearest-even and saturating; the key is projected from the
+// dequantised entry and stored as bf16.
+//
+// quant: one thread per 16-channel group (64 B in, 8 B codes + 1 B scale out),
+//        consecutive threads on consecutive groups, so loads and stores are
+//        contiguous.  fp32 divisions are IEEE correctly rounded (built with
+//        -fhip-fp32-correctly-rounded-divide-sqrt), which makes the codes
+//        bit-identical to any other correct implementation of the same rule.
+// indexer_k: 32 entries per workgroup are dequantised into LDS (fp32, exact),
+//        then each thread accumulates one key channel of several entries in
+//        float64 and rounds once to bf16.
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+
+__global__ __launch_bounds__(256) void quant_fp4_kernel(const float* __restrict__ kv,
+                                                        long long ngroups,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  const float4* src = reinterpret_cast<const float4*>(kv) + g * 4;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float4 v = src[i];
+    x[4 * i + 0] = v.x;
+    x[4 * i + 1] = v.y;
+    x[4 * i + 2] = v.z;
+    x[4 * i + 3] = v.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const uint32_t S = e4m3_encode_nonneg(amax / 6.0f);
+  const float s = e4m3_decode(S);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t c = s > 0.0f ? e2m1_encode(x[i] / s) : ((__float_as_uint(x[i]) >> 28) & 8u);
+    w[i >> 3] |= c << (4 * (i & 7));
+  }
+  reinterpret_cast<uint2*>(codes)[g] = make_uint2(w[0], w[1]);
+  scales[g] = (uint8_t)S;
+}
+
+hipError_t launch_quant_fp4(const float* kv, long long n, int d, uint8_t* codes, uint8_t* scales,
+                            hipStream_t st) {
+  long long ngroups = n * (d / 16);
+  if (ngroups == 0) return hipSuccess;
+  long long blocks = (ngroups + 255) / 256;
+  hipLaunchKernelGGL(quant_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, kv, ngroups, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ indexer key
+
+constexpr int kIkEntries = 32;  // entries per workgroup
+
+template <int DI>
+__global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales,
+                                                        long long n, int d,
+                                                        const uint16_t* __restrict__ W,
+                                                        uint16_t* __restrict__ out) {
+  extern __shared__ float xs[];  // [kIkEntries][d]
+  const long long e0 = (long long)blockIdx.x * kIkEntries;
+  const int slabs = d / 8;
+  for (int t = threadIdx.x; t < kIkEntries * slabs; t += 256) {
+    const int el = t / slabs, sl = t - el * slabs;
+    const long long e = e0 + el;
+    float v[8];
+    if (e < n) {
+      uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + e * (d / 2) + sl * 4);
+      float s = e4m3_decode(scales[e * (d / 16) + (sl >> 1)]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((cw >> (4 * j)) & 15u) * s;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xs[el * d + sl * 8 + j] = v[j];
+  }
+  __syncthreads();
+  constexpr int GRP = 256 / DI;           // entry groups
+  constexpr int PER = kIkEntries / GRP;   // entries per thread
+  const int c = threadIdx.x % DI, grp = threadIdx.x / DI;
+  double acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) acc[p] = 0.0;
+  for (int k = 0; k < d; ++k) {
+    const double wv = (double)bf16_to_f32(W[(size_t)k * DI + c]);
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] = fma((double)xs[(grp + p * GRP) * d + k], wv, acc[p]);
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const long long e = e0 + grp + p * GRP;
+    if (e < n) out[e * DI + c] = (uint16_t)f64_to_bf16_rne(acc[p]);
+  }
+}
+
+hipError_t launch_indexer_k(const uint8_t* codes, const uint8_t* scales, long long n, int d,
+                            const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  long long blocks = (n + kIkEntries - 1) / kIkEntries;
+  size_t lds = (size_t)kIkEntries * d * sizeof(float);
+  if (d_i == 128)
+    hipLaunchKernelGGL(indexer_k_kernel<128>, dim3((unsigned)blocks), dim3(256), lds, st, codes,
+                       scales, n, d, W_ik, k_idx);
+  else
+    hipLaunchKernelGGL(indexer_k_kernel<64>, dim3((unsigned)blocks), dim3(256), lds, st, codes,
+                       scales, n, d, W_ik, k_idx);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

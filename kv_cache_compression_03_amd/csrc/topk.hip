@@ -1,0 +1,438 @@
+// Top-K selection and the shared candidate pool.
+//
+// [deep-dive §3.3] the first Full indexer scans the whole visible range, keeps
+// the best positions of each block and a Top-512; the pool of 2,048 blocks x 8
+// positions is shared by later Reindex layers.  Readings: rank by (score desc,
+// index asc), output ascending and -1 padded; a block is G consecutive entries
+// scored by its maximum; the PB best blocks (ties: lower block) give their PE
+// best entries (ties: lower index).
+//
+// Every ordering is decided on one 64-bit key, (order-preserving bits of the
+// score) << 32 | (0xFFFFFFFF - index): keys are unique, larger is better, and
+// the score ties break to the lower index.
+//
+// Rows with at most kTopkCap visible entries are sorted whole in LDS (one
+// 1024-thread workgroup per row, bitonic).  Longer rows (decode over 64K-1M
+// entries, a handful of rows) first go through two wide passes:
+//   chunkmax: split the row into C >= K chunks and take each chunk's maximum;
+//   filter:   T = min of the chunk maxima.  Those C maxima are C distinct entries
+//             scoring >= T, so the K-th best score is >= T and every entry below
+//             T can be dropped; entries >= T are appended to a candidate list.
+// For continuous scores about K*ln(K) (~3.2K for K = 512) entries survive.  If
+// more than kTopkCap survive (heavy ties), the row falls back to an exact radix
+// select over the whole row in one workgroup (slow, correct).
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+
+constexpr int kSelThreads = 1024;
+
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t topk_ws_bytes(int R, int N, int K) {
+  if (N <= kTopkCap) return 0;
+  size_t b = 0;
+  b += align256((size_t)R * 2 * K * sizeof(float));
+  b += align256((size_t)R * sizeof(int));
+  b += align256((size_t)R * kTopkCap * sizeof(float));
+  b += align256((size_t)R * kTopkCap * sizeof(int));
+  return b;
+}
+
+TopkWs topk_ws_carve(void* ws, int R, int K) {
+  char* p = static_cast<char*>(ws);
+  TopkWs w;
+  w.cmax = reinterpret_cast<float*>(p);
+  p += align256((size_t)R * 2 * K * sizeof(float));
+  w.cnt = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * sizeof(int));
+  w.cscore = reinterpret_cast<float*>(p);
+  p += align256((size_t)R * kTopkCap * sizeof(float));
+  w.cidx = reinterpret_cast<int*>(p);
+  return w;
+}
+
+CSA2_DEV int row_len(const int* valid_len, int r, int N) {
+  if (!valid_len) return N;
+  int v = valid_len[r];
+  return v < 0 ? 0 : (v > N ? N : v);
+}
+
+CSA2_DEV unsigned long long make_key(float s, int idx) {
+  return ((unsigned long long)mono_key(s) << 32) | (0xFFFFFFFFu - (uint32_t)idx);
+}
+CSA2_DEV int key_index(unsigned long long k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+// ---------------------------------------------------------------- wide passes
+
+__global__ __launch_bounds__(256) void topk_chunkmax_kernel(const float* __restrict__ scores, int N,
+                                                            const int* __restrict__ valid_len, int K,
+                                                            float* __restrict__ cmax,
+                                                            int* __restrict__ cnt) {
+  const int r = blockIdx.y;
+  const int n = row_len(valid_len, r, N);
+  if (n <= kTopkCap) return;
+  if (blockIdx.x == 0 && threadIdx.x == 0) cnt[r] = 0;
+  const int clen = n / K;  // >= 4 because n > kTopkCap >= 4K
+  const int C = (n + clen - 1) / clen;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= C) return;
+  const int lane = threadIdx.x & 63;
+  const float* row = scores + (size_t)r * N;
+  const int lo = c * clen, hi = min(lo + clen, n);
+  float mx = -INFINITY;
+  for (int i = lo + lane; i < hi; i += 64) mx = fmaxf(mx, row[i]);
+  mx = wave_max(mx);
+  if (lane == 0) cmax[(size_t)r * 2 * K + c] = mx;
+}
+
+constexpr int kFilterPerThread = 16;
+
+__global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restrict__ scores, int N,
+                                                          const int* __restrict__ valid_len, int K,
+                                                          const float* __restrict__ cmax,
+                                                          int* __restrict__ cnt,
+                                                          float* __restrict__ cscore,
+                                                          int* __restrict__ cidx) {
+  const int r = blockIdx.y;
+  const int n = row_len(valid_len, r, N);
+  if (n <= kTopkCap) return;
+  const long long e0 = (long long)blockIdx.x * 256 * kFilterPerThread;
+  if (e0 >= n) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int clen = n / K;
+  const int C = (n + clen - 1) / clen;
+  __shared__ float red[4];
+  float mn = INFINITY;
+  for (int c = threadIdx.x; c < C; c += 256) mn = fminf(mn, cmax[(size_t)r * 2 * K + c]);
+  mn = wave_min(mn);
+  if (lane == 0) red[wave] = mn;
+  __syncthreads();
+  const uint32_t tk = mono_key(fminf(fminf(red[0], red[1]), fminf(red[2], red[3])));
+  const float* row = scores + (size_t)r * N;
+  for (int it = 0; it < kFilterPerThread; ++it) {
+    const long long e = e0 + it * 256 + threadIdx.x;
+    float s = 0.0f;
+    bool take = false;
+    if (e < n) {
+      s = row[e];
+      take = mono_key(s) >= tk;
+    }
+    const unsigned long long mask = __ballot(take);
+    if (mask) {
+      const int nt = __popcll(mask);
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&cnt[r], nt);
+      base = __shfl(base, 0);
+      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+      if (take && pos < kTopkCap) {
+        cscore[(size_t)r * kTopkCap + pos] = s;
+        cidx[(size_t)r * kTopkCap + pos] = (int)e;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- per-row select
+
+// Bitonic sort of P (power of two) 64-bit keys in LDS, descending.
+CSA2_DEV void bitonic_desc_u64(unsigned long long* a, int P) {
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (P >> 1); i += kSelThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;  // this run ends up descending when up
+        const unsigned long long x = a[lo], y = a[hi];
+        if (up ? (x < y) : (x > y)) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Bitonic sort of P (power of two) ints in LDS, ascending.
+CSA2_DEV void bitonic_asc_i32(int* a, int P) {
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (P >> 1); i += kSelThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int x = a[lo], y = a[hi];
+        if (up ? (x > y) : (x < y)) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+CSA2_DEV int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Exact selection over a whole row in global memory (rows whose candidate list
+// overflowed).  Radix select on the 32-bit score key finds the K-th score T;
+// every entry above T is taken, and entries equal to T are taken in index order
+// until K are chosen.  Writes the chosen indices (unsorted) to sel[0..k).
+CSA2_DEV void radix_select_row(const float* __restrict__ row, int n, int k, int* sel, uint32_t* hist,
+                               int* misc) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint32_t key = mono_key(row[i]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0, dsel = 0;
+      for (int dg = 255; dg >= 0; --dg) {
+        if (acc + (int)hist[dg] >= need) {
+          dsel = dg;
+          break;
+        }
+        acc += (int)hist[dg];
+      }
+      misc[0] = dsel;
+      misc[1] = need - acc;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)misc[0] << shift;
+    pmask |= 255u << shift;
+    need = misc[1];
+    __syncthreads();
+  }
+  // prefix = key of the K-th score; `need` entries equal to it are taken
+  const int n_gt = k - need;
+  if (tid == 0) {
+    misc[2] = 0;  // gt slots used
+    misc[3] = 0;  // equal entries seen so far
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  int* wcount = misc + 8;  // [16]
+  for (int base = 0; base < n; base += kSelThreads) {
+    const int i = base + tid;
+    uint32_t key = 0;
+    if (i < n) key = mono_key(row[i]);
+    const bool gt = i < n && key > prefix;
+    const bool eq = i < n && key == prefix;
+    if (gt) sel[atomicAdd(&misc[2], 1)] = i;
+    const unsigned long long m = __ballot(eq);
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int before = misc[3];
+    for (int w2 = 0; w2 < wave; ++w2) before += wcount[w2];
+    const int rank = before + __popcll(m & ((1ull << lane) - 1ull));
+    if (eq && rank < need) sel[n_gt + rank] = i;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int w2 = 0; w2 < kSelThreads / 64; ++w2) tot += wcount[w2];
+      misc[3] += tot;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, int N, const int* __restrict__ valid_len,
+    const int* __restrict__ cand_map, int K, int* __restrict__ out, const int* __restrict__ cnt,
+    const float* __restrict__ cscore, const int* __restrict__ cidx) {
+  extern __shared__ unsigned long long keys[];  // kTopkCap keys (64 KB)
+  __shared__ int misc[32];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int n = row_len(valid_len, r, N);
+  const bool direct = n <= kTopkCap;
+  const int total = direct ? n : cnt[r];
+  const int k = min(K, direct ? n : min(total, n));
+  const float* row = scores + (size_t)r * N;
+  int* sel;
+  if (!direct && total > kTopkCap) {
+    sel = reinterpret_cast<int*>(keys + 1024);
+    radix_select_row(row, n, k, sel, reinterpret_cast<uint32_t*>(keys), misc);
+  } else {
+    const int P = pow2_at_least(total > 0 ? total : 1);
+    for (int i = tid; i < P; i += kSelThreads) {
+      unsigned long long key = 0ull;
+      if (i < total) {
+        const float s = direct ? row[i] : cscore[(size_t)r * kTopkCap + i];
+        const int idx = direct ? i : cidx[(size_t)r * kTopkCap + i];
+        key = make_key(s, idx);
+      }
+      keys[i] = key;
+    }
+    __syncthreads();
+    bitonic_desc_u64(keys, P);
+    // the chosen indices go to a region the first k keys do not occupy
+    sel = reinterpret_cast<int*>(keys + (P > 4096 ? 6144 : 4096));
+    int idx_tmp[2];
+    int cnt_tmp = 0;
+    for (int i = tid; i < k; i += kSelThreads) idx_tmp[cnt_tmp++] = key_index(keys[i]);
+    __syncthreads();
+    cnt_tmp = 0;
+    for (int i = tid; i < k; i += kSelThreads) sel[i] = idx_tmp[cnt_tmp++];
+  }
+  __syncthreads();
+  const int Pk = pow2_at_least(k > 0 ? k : 1);
+  for (int i = k + tid; i < Pk; i += kSelThreads) sel[i] = 0x7FFFFFFF;
+  __syncthreads();
+  bitonic_asc_i32(sel, Pk);
+  int* orow = out + (size_t)r * K;
+  for (int i = tid; i < K; i += kSelThreads) {
+    int v = -1;
+    if (i < k) v = cand_map ? cand_map[(size_t)r * N + sel[i]] : sel[i];
+    orow[i] = v;
+  }
+}
+
+hipError_t launch_topk(const float* scores, int R, int N, const int* valid_len, const int* cand_map,
+                       int K, int* out_idx, const TopkWs& ws, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  if (N > kTopkCap) {
+    hipLaunchKernelGGL(topk_chunkmax_kernel, dim3((2 * K + 3) / 4, R), dim3(256), 0, st, scores, N,
+                       valid_len, K, ws.cmax, ws.cnt);
+    const int fx = (N + 256 * kFilterPerThread - 1) / (256 * kFilterPerThread);
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(fx, R), dim3(256), 0, st, scores, N, valid_len, K,
+                       ws.cmax, ws.cnt, ws.cscore, ws.cidx);
+  }
+  hipLaunchKernelGGL(topk_select_kernel, dim3(R), dim3(kSelThreads),
+                     kTopkCap * sizeof(unsigned long long), st, scores, N, valid_len, cand_map, K,
+                     out_idx, ws.cnt, ws.cscore, ws.cidx);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- candidate pool
+
+static inline int pool_nblk(int N, int G) { return (N + G - 1) / G; }
+
+size_t pool_ws_bytes(int R, int N, int G, int PB) {
+  const int nb = pool_nblk(N, G);
+  size_t b = 0;
+  b += align256((size_t)R * nb * sizeof(float));  // block maxima
+  b += align256((size_t)R * sizeof(int));         // blocks per row
+  b += align256((size_t)R * PB * sizeof(int));    // chosen blocks
+  b += topk_ws_bytes(R, nb, PB);
+  return b;
+}
+
+CSA2_DEV int visible(const int* q_pos, int m, int r, int N) {
+  if (!q_pos) return N;
+  long long v = ((long long)q_pos[r] + 1) / m;
+  return (int)(v < 0 ? 0 : (v > N ? N : v));
+}
+
+__global__ __launch_bounds__(256) void pool_blockmax_kernel(const float* __restrict__ scores, int N,
+                                                            const int* __restrict__ q_pos, int m,
+                                                            int G, int nblk_max,
+                                                            float* __restrict__ bmax,
+                                                            int* __restrict__ nblk_out) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblk_max) return;
+  const int n = visible(q_pos, m, r, N);
+  const int nblk = (n + G - 1) / G;
+  if (blk == 0 && lane == 0) nblk_out[r] = nblk;
+  float mx = -INFINITY;
+  if (blk < nblk) {
+    const float* row = scores + (size_t)r * N;
+    const int lo = blk * G, hi = min(lo + G, n);
+    for (int i = lo + lane; i < hi; i += 64) mx = fmaxf(mx, row[i]);
+    mx = wave_max(mx);
+  }
+  if (lane == 0) bmax[(size_t)r * nblk_max + blk] = mx;
+}
+
+__global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restrict__ scores, int N,
+                                                          const int* __restrict__ q_pos, int m, int G,
+                                                          int PB, int PE,
+                                                          const int* __restrict__ selblk,
+                                                          int* __restrict__ pool,
+                                                          int* __restrict__ pool_len) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= PB) return;
+  const int n = visible(q_pos, m, r, N);
+  const int nblk = (n + G - 1) / G;
+  const int nsel = min(PB, nblk);
+  int* prow = pool + (size_t)r * PB * PE;
+  if (slot >= nsel) {
+    for (int i = lane; i < PE; i += 64) prow[(size_t)slot * PE + i] = -1;
+    if (slot == 0 && lane == 0) pool_len[r] = 0;
+    return;
+  }
+  const int blk = selblk[(size_t)r * PB + slot];
+  const int lo = blk * G;
+  const int len = min(G, n - lo);
+  const float* row = scores + (size_t)r * N;
+  unsigned long long key[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = lane + 64 * q;
+    key[q] = j < len ? make_key(row[lo + j], lo + j) : 0ull;
+  }
+  const int cntb = min(PE, len);  // PE <= 16
+  int mine = 0x7FFFFFFF;          // lane p keeps the p-th pick
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    if (p < cntb) {
+      unsigned long long best = key[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
+      best = wave_max_u64(best);
+      if (lane == p) mine = key_index(best);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (key[q] == best) key[q] = 0ull;
+    }
+  }
+  // ascending order of the picks: rank = number of smaller picks
+  int rank = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int v = __shfl(mine, q);
+    rank += (q < cntb && v < mine) ? 1 : 0;
+  }
+  if (lane < cntb) prow[(size_t)slot * PE + rank] = mine;
+  else if (lane < PE) prow[(size_t)slot * PE + lane] = -1;
+  if (slot == nsel - 1 && lane == 0) pool_len[r] = slot * PE + cntb;
+}
+
+hipError_t launch_pool(const float* scores, int R, int N, const int* q_pos, int m, int G, int PB,
+                       int PE, int* pool, int* pool_len, void* ws, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  const int nb = pool_nblk(N, G);
+  char* p = static_cast<char*>(ws);
+  float* bmax = reinterpret_cast<float*>(p);
+  p += align256((size_t)R * nb * sizeof(float));
+  int* nblk = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * sizeof(int));
+  int* selblk = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * PB * sizeof(int));
+  TopkWs tws = topk_ws_carve(p, R, PB);
+  hipLaunchKernelGGL(pool_blockmax_kernel, dim3((nb + 3) / 4, R), dim3(256), 0, st, scores, N, q_pos,
+                     m, G, nb, bmax, nblk);
+  hipError_t e = launch_topk(bmax, R, nb, nblk, nullptr, PB, selblk, tws, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pool_gather_kernel, dim3((PB + 3) / 4, R), dim3(256), 0, st, scores, N, q_pos, m,
+                     G, PB, PE, selblk, pool, pool_len);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

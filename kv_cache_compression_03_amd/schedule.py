@@ -1,0 +1,112 @@
+"""Decode step of a Full / Reindex / Reuse layer schedule on the CSA2 library.
+
+[deep-dive §3.2] every attention layer is statically Full (fresh indexer scores
+and Top-K; the first Full layer of a step also builds the shared candidate pool,
+§3.3), Reindex (fresh scores over the pool only) or Reuse (the most recent
+selection, no indexer); every layer attends with its own main query and its own
+window [reading §4.2].  The decoder schedule is Full + 3 Reuse, then four groups
+of Reindex + 3 Reuse.
+
+All buffers are allocated once, so a step can be captured into a HIP graph and
+replayed.  Layers run in order on one stream (in a model, layer l+1's queries
+depend on layer l's output, so layers are never fused).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import binding as bd
+
+FULL, REINDEX, REUSE, SWA_ONLY = "F", "R", "U", "S"
+
+
+@dataclass
+class LayerBuffers:
+    """Per-layer inputs on the device: main query [B,1,H_q,d] bf16, window [B,S,d]
+    E4M3 bytes and, for Full/Reindex layers, indexer query [B,1,h_i,d_i] bf16 and
+    head weights [B,1,h_i] f32."""
+    q_main: torch.Tensor
+    swa: torch.Tensor
+    q_idx: Optional[torch.Tensor] = None
+    w: Optional[torch.Tensor] = None
+
+
+class DecodeSchedule:
+    def __init__(self, schedule: Sequence[str], B: int, N: int, d: int, h_i: int, d_i: int,
+                 H_q: int, S: int, K: int = 512, G: int = 128, PB: int = 2048, PE: int = 8,
+                 swa_scale: float = 1.0, device: str = "cuda"):
+        self.layers: List[str] = list(schedule)
+        for i, mode in enumerate(self.layers):
+            if mode not in (FULL, REINDEX, REUSE, SWA_ONLY):
+                raise ValueError(f"layer {i}: unknown mode {mode!r}")
+            if mode in (REUSE,) and not any(x in (FULL, REINDEX) for x in self.layers[:i]):
+                raise ValueError(f"layer {i}: Reuse before any Full/Reindex layer")
+            if mode == REINDEX and FULL not in self.layers[:i]:
+                raise ValueError(f"layer {i}: Reindex before any Full layer")
+        self.B, self.N, self.d, self.h_i, self.d_i = B, N, d, h_i, d_i
+        self.H_q, self.S, self.K, self.G, self.PB, self.PE = H_q, S, K, G, PB, PE
+        self.swa_scale = swa_scale
+        self.need_pool = REINDEX in self.layers
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.scores = torch.empty(B, 1, N, dtype=torch.float32, device=dev)
+        self.sel: Dict[int, torch.Tensor] = {i: torch.empty(B, 1, K, **i32)
+                                             for i, m in enumerate(self.layers) if m in (FULL, REINDEX)}
+        self.no_sel = torch.full((B, 1, K), -1, **i32)
+        self.pool = torch.empty(B, PB * PE, **i32) if self.need_pool else None
+        self.pool_len = torch.empty(B, **i32) if self.need_pool else None
+        self.out = [torch.empty(B, 1, H_q, d, dtype=torch.float32, device=dev) for _ in self.layers]
+        ws = max(bd.csa2_index_full_workspace(B, 1, N, G, PB, PE) if self.need_pool else 0,
+                 bd.csa2_topk_workspace(B, N, K),
+                 bd.csa2_index_reindex_workspace(B, PB * PE, K) if self.need_pool else 0,
+                 bd.csa2_sparse_attn_workspace(B, 1, H_q, d, K, S))
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+
+    def selection_of(self, layer: int) -> torch.Tensor:
+        """The selection layer `layer` attends to (Reuse: the most recent Full/Reindex)."""
+        if self.layers[layer] == SWA_ONLY:
+            return self.no_sel
+        for j in range(layer, -1, -1):
+            if j in self.sel:
+                return self.sel[j]
+        raise ValueError("no selection")
+
+    def step(self, codes: torch.Tensor, scales: torch.Tensor, k_idx: torch.Tensor,
+             layers: Sequence[LayerBuffers], stream=None) -> List[torch.Tensor]:
+        """One decode query per sequence through every layer; returns the per-layer outputs."""
+        B, K = self.B, self.K
+        pool_built = False
+        for i, (mode, lb) in enumerate(zip(self.layers, layers)):
+            if mode == FULL:
+                build = self.need_pool and not pool_built
+                bd.csa2_index_full(lb.q_idx, lb.w, k_idx, scores=self.scores,
+                                   pool=self.pool if build else None,
+                                   pool_len=self.pool_len if build else None,
+                                   G=self.G, PB=self.PB, PE=self.PE, ws=self.ws, stream=stream)
+                pool_built = pool_built or build
+                bd.csa2_topk(self.scores.view(B, self.N), K, out=self.sel[i].view(B, K), ws=self.ws,
+                             stream=stream)
+            elif mode == REINDEX:
+                bd.csa2_index_reindex(lb.q_idx.view(B, self.h_i, self.d_i), lb.w.view(B, self.h_i),
+                                      k_idx, self.pool, self.pool_len, K,
+                                      sel=self.sel[i].view(B, K), ws=self.ws, stream=stream)
+            bd.csa2_sparse_attn(lb.q_main, codes, scales, self.selection_of(i), lb.swa,
+                                swa_scale=self.swa_scale, out=self.out[i], ws=self.ws,
+                                stream=stream)
+        return self.out
+
+    def capture(self, codes, scales, k_idx, layers, warmup: int = 1) -> torch.cuda.CUDAGraph:
+        """Capture one step into a graph (after `warmup` eager steps on a side stream)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(warmup):
+                self.step(codes, scales, k_idx, layers)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(codes, scales, k_idx, layers)
+        return g

@@ -1,0 +1,79 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments before touching the GPU (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "csa2.h")
+LIB = os.path.join(ROOT, "kv_cache_compression_03_amd", "libcsa2.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libcsa2.so not built")
+
+
+def declared():
+    txt = open(HDR).read()
+    return sorted(set(re.findall(r"CSA2_API\s+[\w\s\*]+?\b(csa2_\w+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    from kv_cache_compression_03_amd import binding
+    L = binding.lib()
+    names = declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in binding.csa2_version()
+
+
+def test_workspace_queries_are_host_only():
+    from kv_cache_compression_03_amd import binding as bd
+    assert bd.csa2_topk_workspace(4, 4096, 512) == 0          # rows sorted whole in LDS
+    assert bd.csa2_topk_workspace(8, 1 << 20, 512) > 8 * 8192 * 8
+    assert bd.csa2_index_reindex_workspace(8, 16384, 512) >= 8 * 16384 * 4
+    assert bd.csa2_index_full_workspace(8, 1, 1 << 20, 128, 2048, 8) >= 8 * 8192 * 4
+    assert bd.csa2_sparse_attn_workspace(8192, 1, 64, 512, 512, 8319) == 0   # one split
+    assert bd.csa2_sparse_attn_workspace(8, 1, 64, 512, 512, 128) > 0
+
+
+def test_status_strings():
+    from kv_cache_compression_03_amd import binding as bd
+    L = bd.lib()
+    assert L.csa2_status_string(0) == b"ok"
+    assert L.csa2_status_string(3) == b"workspace too small"
+
+
+def _fake(addr=1 << 20):
+    return ctypes.c_void_p(addr)
+
+
+def test_invalid_arguments_rejected_before_launch():
+    from kv_cache_compression_03_amd import binding as bd
+    L = bd.lib()
+    p = _fake()
+    # null pointer
+    st = L.csa2_quant_fp4(None, 16, 512, p, p, None, 0, None, None)
+    assert st == 1 and b"kv is null" in L.csa2_last_error()
+    # misaligned pointer
+    st = L.csa2_quant_fp4(_fake((1 << 20) + 4), 16, 512, p, p, None, 0, None, None)
+    assert st == 1 and b"aligned" in L.csa2_last_error()
+    # unsupported dims
+    assert L.csa2_quant_fp4(p, 16, 40, p, p, None, 0, None, None) == 2
+    assert L.csa2_sparse_attn(p, p, p, 10, p, 8, p, 1.0, 4, 0, 128, None, 1, 1, 24, 512, 0.0,
+                              p, None, None, 0, None) == 2                      # H_q % 16
+    assert L.csa2_topk(p, 1, 10, None, None, 4096, p, None, 0, None) == 2        # K > 2048
+    assert L.csa2_index_full(p, p, p, 1, 1, 10, 6, 128, None, 1, p, None, None, 128, 2048, 8,
+                             None, 0, None) == 2                                 # h_i
+    # workspace too small
+    assert L.csa2_topk(p, 8, 1 << 20, None, None, 512, p, None, 0, None) == 3
+    assert b"workspace" in L.csa2_last_error()
+    assert L.csa2_index_reindex(p, p, p, p, p, 4, 16384, 1 << 20, 8, 128, 512, p, p, 16, None) == 3
+    # compressor limits
+    assert L.csa2_compress(p, 0, 1, 8, 64, p, p, 0, 256, 256, 3, 0, 64, 1e4, p, None) == 2   # m = 3
+    assert L.csa2_compress(p, 0, 1, 8, 64, p, p, 1, 256, 256, 2, 0, 64, 1e4, p, None) == 2   # dtypes
+    assert L.csa2_compress(p, 0, 1, 8, 64, p, p, 0, 256, 256, 2, 1, 64, 1e4, p, None) == 1   # pos0 % m
+    # empty work is a no-op success
+    assert L.csa2_quant_fp4(None, 0, 512, None, None, None, 0, None, None) == 0
+    assert L.csa2_last_error() == b""
