@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of one CSA2 decode step on one MI355X.
+
+A step = one decode query per sequence through the workload's whole layer
+schedule (indexer scan + Top-K for Full layers, pool rescoring for Reindex
+layers, sparse attention in every layer), replayed from a captured HIP graph.
+Inputs (FP4 main KV, indexer keys, per-layer queries and windows) are built and
+resident in HBM before the timed region.
+
+Prints one JSON line.  Default workload: 64 sequences x 65,536 entries,
+[Full + Reuse x 3].
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "CSA2 decode queries/s at 64K–1M ctx; achieved HBM GB/s vs MI355X peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_64k_b64")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "kv_cache_compression_03_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes a step must move at least: every Full layer streams the indexer keys
+    of all entries; a Reindex layer gathers the keys of its pool; every layer reads
+    its selected FP4 entries, its window, its query and writes its output."""
+    entry = wl.d // 2 + wl.d // 16          # FP4 codes + E4M3 scales
+    ik = wl.d_i * 2
+    per_attn = wl.K * entry + wl.S * wl.d + wl.H_q * wl.d * 2 + wl.H_q * wl.d * 4
+    layers = wl.layers
+    full = layers.count("F") * wl.B * wl.N * ik
+    reidx = layers.count("R") * wl.B * wl.PB * wl.PE * ik
+    attn = len(layers) * wl.B * per_attn
+    return {"full_scan": full, "reindex": reidx, "attention": attn, "total": full + reidx + attn}
+
+
+def build_inputs(wl, torch, bd, sch):
+    import synth
+    dev = torch.device("cuda")
+    B, N, d = wl.B, wl.N, wl.d
+    codes = torch.empty(B, N, d // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(B, N, d // 16, dtype=torch.uint8, device=dev)
+    kidx = torch.empty(B, N, wl.d_i, dtype=torch.bfloat16, device=dev)
+    W = torch.from_numpy(synth.w_ik(wl).view(np.int16)).view(torch.bfloat16).to(dev)
+    t0 = time.time()
+    workers = min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(workers) as ex:
+        futs = [ex.submit(synth.main_kv, wl, b) for b in range(B)]
+        for b, f in enumerate(futs):
+            x = torch.from_numpy(f.result()).to(dev)
+            bd.csa2_quant_fp4(x, codes=codes[b], scales=scales[b], W_ik=W, k_idx=kidx[b])
+            del x
+    torch.cuda.synchronize()
+    log(f"cache built: {B} x {N} entries in {time.time() - t0:.1f}s")
+    layers = []
+    for li, mode in enumerate(wl.layers):
+        qm = np.stack([synth.q_main(wl, li, b) for b in range(B)])
+        sw = np.stack([synth.swa_tokens(wl, li, b) for b in range(B)])
+        qi = w = None
+        if mode in "FR":
+            qi = np.stack([synth.q_index(wl, li, b) for b in range(B)])
+            w = np.stack([synth.head_weights(wl, li, b) for b in range(B)])
+        tb = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        layers.append(sch.LayerBuffers(tb(qm), tt(sw), None if qi is None else tb(qi),
+                                       None if w is None else tt(w)))
+    return codes, scales, kidx, layers
+
+
+def time_scan(wl, torch, bd, kidx, layers, reps):
+    """Average duration of the indexer-scan kernel launch (the dominant kernel),
+    measured with HIP events on the stream it is launched on."""
+    st = torch.cuda.current_stream()
+    scores = torch.empty(wl.B, 1, wl.N, dtype=torch.float32, device="cuda")
+    lb = layers[0]
+    for _ in range(3):
+        bd.csa2_index_full(lb.q_idx, lb.w, kidx, scores=scores)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        bd.csa2_index_full(lb.q_idx, lb.w, kidx, scores=scores)
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps / 1e3  # seconds
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload: the
+    decode step of 2 sequences, repeated until `seconds` of CPU work."""
+    import synth
+    from oracle.csa2 import LayerInputs, decode_step, indexer_k, quant_fp4
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    W = synth.w_ik(wl)
+    seqs = []
+    for b in range(2):
+        q8 = quant_fp4(synth.main_kv(wl, b))
+        k = indexer_k(q8.codes, q8.scales, W)
+        lays = []
+        for li, mode in enumerate(wl.layers):
+            lays.append(LayerInputs(synth.q_main(wl, li, b)[0], synth.swa_tokens(wl, li, b),
+                                    synth.q_index(wl, li, b)[0] if mode in "FR" else None,
+                                    synth.head_weights(wl, li, b)[0] if mode in "FR" else None))
+        seqs.append((q8, k, lays))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        q8, k, lays = seqs[n % 2]
+        decode_step(wl.layers, lays, q8.codes, q8.scales, k, K=wl.K, G=wl.G, PB=wl.PB, PE=wl.PE)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} decode steps of sequences 0-1 of {wl.name} "
+                      f"({'+'.join(wl.layers)}, {wl.N} entries), {el:.1f}s, float64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not "
+              "part of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from kv_cache_compression_03_amd import binding as bd
+    from kv_cache_compression_03_amd import schedule as sch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bd.lib()
+    wl = synth.workload(args.workload)
+    if wl.T:
+        raise SystemExit("workloads built from hidden states are parity cases, not bench lines")
+    log(f"workload {wl.name}: B={wl.B} N={wl.N} d={wl.d} schedule={wl.schedule}")
+    codes, scales, kidx, layers = build_inputs(wl, torch, bd, sch)
+    run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
+                             G=wl.G, PB=wl.PB, PE=wl.PE)
+    if args.no_graph:
+        step = lambda: run.step(codes, scales, kidx, layers)
+    else:
+        g = run.capture(codes, scales, kidx, layers)
+        step = g.replay
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    log(f"timed {args.steps} steps: {step_s * 1e6:.1f} us/step (wall {t_wall / args.steps * 1e6:.1f} us)")
+
+    ab = algorithmic_bytes(wl)
+    scan_s = time_scan(wl, torch, bd, kidx, layers, args.kernel_reps)
+    scan_bytes = wl.B * wl.N * wl.d_i * 2
+    achieved = scan_bytes / scan_s / 1e9
+    log(f"scan kernel: {scan_s * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_index_scores_{wl.name}.json")
+    if os.path.exists(tf):
+        with open(tf) as f:
+            rec = json.load(f)
+        if rec.get("source_sha") == source_sha("index.hip", "common.h"):
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": wl.B / step_s,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "sequences": wl.B, "context_entries": wl.N, "m": wl.m,
+                   "d": wl.d, "indexer": f"{wl.h_i}x{wl.d_i}", "heads": wl.H_q, "window": wl.S,
+                   "top_k": wl.K, "schedule": wl.schedule,
+                   "graph": not args.no_graph, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "index_scores_kernel (Full-layer indexer scan)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "launch_us": scan_s * 1e6, "algorithmic_bytes_per_launch": scan_bytes},
+        "step_hbm": {"algorithmic_bytes": ab["total"], "GB_s": ab["total"] / step_s / 1e9,
+                     "frac": ab["total"] / step_s / 1e9 / HBM_PEAK_GBS, "breakdown": ab},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

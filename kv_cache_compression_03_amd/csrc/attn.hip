@@ -9,19 +9,23 @@
 // All H_q heads share each key, so per query the work is a dense
 // [H_q x d]·[d x keys] and [H_q x keys]·[keys x d] pair: at 64 heads it is about
 // 200 flops per byte of keys, so both products run on MFMA (16x16x32 bf16):
-//   * a workgroup owns one query row, 16*WAVES heads (one wave per 16 heads) and
-//     a contiguous range of 32-key chunks (split-K over the keys);
+//   * a workgroup owns one query row, up to 64 heads and a contiguous range of
+//     32-key chunks (split-K over the keys); its waves are (16-head group) x
+//     (half of the output dims), so Q and O each take 64 registers per lane and
+//     two waves fit per SIMD;
 //   * per chunk the workgroup dequantises the 32 keys once into LDS, exactly, as
-//     bf16 (E2M1 x E4M3 and E4M3 values fit bf16), in two layouts: key-major for
-//     S^T = K·Q^T and dim-major for O += P·V;
+//     bf16 (E2M1 x E4M3 and E4M3 values fit bf16; hardware FP4/FP8 conversions),
+//     in two layouts: key-major for S^T = K·Q^T and dim-major for O += P·V; the
+//     next chunk's bytes are loaded while the current chunk is multiplied;
 //   * S^T puts heads on MFMA columns, so each lane owns one head's 8 logits and
 //     the softmax row reductions are two cross-lane steps; the probabilities in
 //     that layout are directly the A operand of P·V (the key order inside the
 //     reduction is permuted consistently in P and V);
 //   * P is split into bf16 hi + lo parts (two MFMAs), so P·V keeps ~16 bits of
 //     the fp32 probabilities; logits and sums stay in fp32;
-//   * online softmax in base 2; per-split (O, m, l) partials are merged by a
-//     small combine kernel (or written directly when there is one split).
+//   * online softmax in base 2 against a lazily moved reference maximum; per-split
+//     (O, m, l) partials are merged by a small combine kernel (or written
+//     directly when there is one split).
 #include "common.h"
 #include "internal.h"
 
@@ -31,19 +35,27 @@ constexpr int kKC = 32;  // keys per chunk
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Waves of a workgroup: HG head groups of 16 heads x DS halves of the output dims.
+static inline void attn_shape(int H_q, int d, int& hg, int& ds) {
+  const int hpw = H_q / 16;
+  hg = (hpw % 4 == 0) ? 4 : ((hpw % 2 == 0) ? 2 : 1);
+  ds = 2;
+  (void)d;
+}
+
 AttnPlan attn_plan(int B, int Tq, int H_q, int K, int L_max) {
   AttnPlan p;
-  const int hpw = H_q / 16;
-  p.waves = (hpw % 4 == 0) ? 4 : ((hpw % 2 == 0) ? 2 : 1);
-  p.head_groups = hpw / p.waves;
+  int hg, ds;
+  attn_shape(H_q, 0, hg, ds);
+  p.waves = hg * ds;
+  p.head_groups = (H_q / 16) / hg;
   const long long base = (long long)B * Tq * p.head_groups;
-  const int max_chunks = (L_max + kKC - 1) / kKC;
+  const int max_chunks = (L_max + kKC - 1) / kKC + 1;  // +1: a chunk holds one kind of key
   long long want = (256 + base - 1) / base;
   int ns = (int)(want < 1 ? 1 : (want > max_chunks ? max_chunks : want));
-  if (ns < 1) ns = 1;
   p.chunks_per_split = (max_chunks + ns - 1) / ns;
   if (p.chunks_per_split < 1) p.chunks_per_split = 1;
-  p.n_splits = max_chunks > 0 ? (max_chunks + p.chunks_per_split - 1) / p.chunks_per_split : 1;
+  p.n_splits = (max_chunks + p.chunks_per_split - 1) / p.chunks_per_split;
   return p;
 }
 
@@ -55,29 +67,39 @@ size_t attn_ws_bytes(int B, int Tq, int H_q, int d, int K, int L_max) {
          align256(rows * p.n_splits * H_q * 2 * sizeof(float));
 }
 
-template <int D, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void sparse_attn_kernel(
+// Softmax state is kept against a reference maximum that only moves when a new
+// logit exceeds it by more than 2^kLazy (log2 units), so O is rarely rescaled;
+// probabilities stay below 2^kLazy, far inside float range.
+constexpr float kLazy = 8.0f;
+
+template <int D, int HG>
+__global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int N, const int* __restrict__ sel, int K,
     const uint8_t* __restrict__ swa, float swa_scale, int S, long long swa_pos0, int n_win,
     const int* __restrict__ q_pos, int Tq, int H_q, float sm_log2, int chunks_per_split,
     int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml,
     float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int NT = WAVES * 64;
-  constexpr int KSTR = D + 8;     // key-major row stride (bf16): 16 B pad
-  constexpr int VSTR = kKC + 4;   // dim-major row stride (bf16): 72 B
+  constexpr int DS = 2;                       // output-dim halves
+  constexpr int NT = HG * DS * 64;
+  constexpr int DH = D / DS;                  // output dims per wave
+  constexpr int KSTR = D + 8;                 // key-major row stride (bf16): 16 B pad
+  constexpr int VSTR = kKC + 4;               // dim-major row stride (bf16): 72 B
+  constexpr int NB = (kKC / 4) * (D / 8);     // 4-key x 8-dim dequantisation blocks
+  constexpr int ITER = (NB + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint16_t Krow[kKC * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
-  __shared__ int s_src[kKC];      // >= 0 entry, <= -2 window token (-2 - row), -1 none
+  __shared__ int s_sel[2048];
   __shared__ float s_ksc[kKC];
+  __shared__ int s_valid[kKC];
   __shared__ int s_nsel;
 
-  const int split = blockIdx.x, row = blockIdx.y, hg = blockIdx.z;
+  const int split = blockIdx.x, row = blockIdx.y, hgrp = blockIdx.z;
   const int b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
-  const int head0 = (hg * WAVES + wave) * 16;
+  const int head0 = (hgrp * HG + (wave % HG)) * 16;
+  const int dim0 = (wave / HG) * DH;
 
-  // valid selections form a prefix (ascending list padded with -1)
   const int* srow = sel + (size_t)row * K;
   if (tid == 0) s_nsel = 0;
   __syncthreads();
@@ -87,7 +109,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attn_kernel(
   for (int o = 32; o > 0; o >>= 1) cv += __shfl_xor(cv, o);
   if (lane == 0) atomicAdd(&s_nsel, cv);
   __syncthreads();
-  const int n_sel = s_nsel;
+  const int n_sel = N > 0 ? s_nsel : 0;
 
   int swa_lo = 0, n_swa = S;
   if (q_pos != nullptr) {
@@ -98,10 +120,49 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attn_kernel(
     swa_lo = (int)lo;
     n_swa = hi > lo ? (int)(hi - lo) : 0;
   }
-  const int L = n_sel + n_swa;
-  const int n_chunks = (L + kKC - 1) / kKC;
+  // chunks hold keys of one kind: first the selected entries, then the window
+  const int nm = (n_sel + kKC - 1) / kKC;
+  const int n_chunks = nm + (n_swa + kKC - 1) / kKC;
   const int c_begin = split * chunks_per_split;
   const int c_end = min(n_chunks, c_begin + chunks_per_split);
+  const int sl_lo = c_begin * kKC;
+  const int sl_hi = min(min(c_end, nm) * kKC, n_sel);
+  for (int i = sl_lo + tid; i < sl_hi; i += NT) s_sel[i - sl_lo] = srow[i];
+  __syncthreads();
+
+  // raw bytes of one chunk: per 4-key x 8-dim block, ra = 4 code bytes (or window
+  // bytes 0-3), rb = the scale byte (or window bytes 4-7)
+  uint32_t ra[ITER][4], rb[ITER][4];
+  auto load_chunk = [&](int c) {
+    const bool main = c < nm;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int bid = tid + it * NT;
+      if (bid < NB) {
+        const int kq = bid / (D / 8), dg = bid - kq * (D / 8);
+        if (main) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int slot = c * kKC + 4 * kq + j;
+            int e = slot < n_sel ? s_sel[slot - sl_lo] : 0;
+            e = (e >= 0 && e < N) ? e : 0;
+            const size_t ent = (size_t)b * N + e;
+            ra[it][j] = *reinterpret_cast<const uint32_t*>(codes + ent * (D / 2) + 4 * dg);
+            rb[it][j] = scales[ent * (D / 16) + (dg >> 1)];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = (c - nm) * kKC + 4 * kq + j;
+            const size_t tok = (size_t)b * S + swa_lo + (t < n_swa ? t : 0);
+            const uint2 raw = *reinterpret_cast<const uint2*>(swa + tok * D + 8 * dg);
+            ra[it][j] = raw.x;
+            rb[it][j] = raw.y;
+          }
+        }
+      }
+    }
+  };
 
   bf16x8_t qb[D / 32];
   {
@@ -109,79 +170,71 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attn_kernel(
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) qb[s] = as_bf16x8(qr[4 * s + g]);
   }
-  f32x4_t o[D / 16];
+  f32x4_t o[DH / 16];
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int n = 0; n < DH / 16; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.0f;
 
+  if (c_begin < c_end) load_chunk(c_begin);
   for (int c = c_begin; c < c_end; ++c) {
-    __syncthreads();
+    const bool main = c < nm;
+    __syncthreads();  // the previous chunk's LDS reads are done
     if (tid < kKC) {
-      const int slot = c * kKC + tid;
-      int src = -1;
-      float ksc = 0.0f;
-      if (slot < n_sel) {
-        const int e = srow[slot];
-        if (e >= 0 && e < N) {
-          src = e;
-          ksc = 1.0f;
-        }
-      } else if (slot < L) {
-        src = -2 - (swa_lo + (slot - n_sel));
-        ksc = swa_scale;
+      bool valid;
+      if (main) {
+        const int slot = c * kKC + tid;
+        const int e = slot < n_sel ? s_sel[slot - sl_lo] : -1;
+        valid = e >= 0 && e < N;
+      } else {
+        valid = (c - nm) * kKC + tid < n_swa;
       }
-      s_src[tid] = src;
-      s_ksc[tid] = ksc;
+      s_valid[tid] = valid ? 1 : 0;
+      s_ksc[tid] = valid ? (main ? 1.0f : swa_scale) : 0.0f;
     }
-    __syncthreads();
-    // ---- dequantise 32 keys into both LDS layouts; a thread owns 8 keys x 8 dims
-    for (int bid = tid; bid < (kKC / 8) * (D / 8); bid += NT) {
-      const int kg = bid / (D / 8), dg = bid - kg * (D / 8);
-      uint32_t v[8][4];
+    // ---- dequantise (exactly, to bf16) into the key-major and dim-major layouts
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int src = s_src[8 * kg + j];
-        if (src >= 0) {
-          const size_t ent = (size_t)b * N + src;
-          const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + ent * (D / 2) + 4 * dg);
-          const float sc = e4m3_decode(scales[ent * (D / 16) + (dg >> 1)]);
+    for (int it = 0; it < ITER; ++it) {
+      const int bid = tid + it * NT;
+      if (bid < NB) {
+        const int kq = bid / (D / 8), dg = bid - kq * (D / 8);
+        uint32_t v[4][4];  // [key][dim pair] packed bf16 pairs
+        if (main) {
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const float lo = e2m1_decode((cw >> (8 * p)) & 15u) * sc;
-            const float hi = e2m1_decode((cw >> (8 * p + 4)) & 15u) * sc;
-            v[j][p] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-          }
-        } else if (src <= -2) {
-          const size_t tok = (size_t)b * S + (size_t)(-2 - src);
-          const uint2 raw = *reinterpret_cast<const uint2*>(swa + tok * D + 8 * dg);
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t wd = p < 2 ? raw.x : raw.y;
-            const uint32_t b0 = (wd >> (16 * (p & 1))) & 0xFFu, b1 = (wd >> (16 * (p & 1) + 8)) & 0xFFu;
-            v[j][p] = e4m3_to_bf16(b0) | (e4m3_to_bf16(b1) << 16);
+          for (int j = 0; j < 4; ++j) {
+            const float sc = e4m3_decode(rb[it][j]);
+            const uint32_t cw = ra[it][j];
+            f32x2_t x;
+            x = fp4x2_to_f32<0>(cw); v[j][0] = pack_hi16(x[0] * sc, x[1] * sc);
+            x = fp4x2_to_f32<1>(cw); v[j][1] = pack_hi16(x[0] * sc, x[1] * sc);
+            x = fp4x2_to_f32<2>(cw); v[j][2] = pack_hi16(x[0] * sc, x[1] * sc);
+            x = fp4x2_to_f32<3>(cw); v[j][3] = pack_hi16(x[0] * sc, x[1] * sc);
           }
         } else {
 #pragma unroll
-          for (int p = 0; p < 4; ++p) v[j][p] = 0u;
+          for (int j = 0; j < 4; ++j) {
+            v[j][0] = e4m3x2_to_bf16x2<false>(ra[it][j]);
+            v[j][1] = e4m3x2_to_bf16x2<true>(ra[it][j]);
+            v[j][2] = e4m3x2_to_bf16x2<false>(rb[it][j]);
+            v[j][3] = e4m3x2_to_bf16x2<true>(rb[it][j]);
+          }
         }
-      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint4*>(&Krow[(8 * kg + j) * KSTR + 8 * dg]) =
-            make_uint4(v[j][0], v[j][1], v[j][2], v[j][3]);
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint4*>(&Krow[(4 * kq + j) * KSTR + 8 * dg]) =
+              make_uint4(v[j][0], v[j][1], v[j][2], v[j][3]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int sh = 16 * (i & 1), p = i >> 1;
-        uint32_t wds[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          wds[jj] = ((v[2 * jj][p] >> sh) & 0xFFFFu) | (((v[2 * jj + 1][p] >> sh) & 0xFFFFu) << 16);
-        uint2* dst = reinterpret_cast<uint2*>(&Vt[(8 * dg + i) * VSTR + 8 * kg]);
-        dst[0] = make_uint2(wds[0], wds[1]);
-        dst[1] = make_uint2(wds[2], wds[3]);
+        for (int i = 0; i < 8; ++i) {
+          // dim 8dg+i of keys 4kq..4kq+3: low halves for even i, high halves for odd i
+          const uint32_t sel2 = (i & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t w0 = __builtin_amdgcn_perm(v[1][i >> 1], v[0][i >> 1], sel2);
+          const uint32_t w1 = __builtin_amdgcn_perm(v[3][i >> 1], v[2][i >> 1], sel2);
+          *reinterpret_cast<uint2*>(&Vt[(8 * dg + i) * VSTR + 4 * kq]) = make_uint2(w0, w1);
+        }
       }
     }
     __syncthreads();
+    // the next chunk's loads fly while this chunk is multiplied
+    if (c + 1 < c_end) load_chunk(c + 1);
 
     // ---- S^T = K·Q^T: rows = keys (two 16-key tiles), columns = this wave's heads
     f32x4_t st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
@@ -199,39 +252,38 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attn_kernel(
       const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
       ks[i] = s_ksc[k0];
       ks[4 + i] = s_ksc[k1];
-      lg[i] = s_src[k0] != -1 ? st0[i] * ks[i] * sm_log2 : -INFINITY;
-      lg[4 + i] = s_src[k1] != -1 ? st1[i] * ks[4 + i] * sm_log2 : -INFINITY;
+      lg[i] = s_valid[k0] ? st0[i] * ks[i] * sm_log2 : -INFINITY;
+      lg[4 + i] = s_valid[k1] ? st1[i] * ks[4 + i] * sm_log2 : -INFINITY;
     }
     float cmax = lg[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, lg[i]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    float alpha = 1.0f, p[8], psum = 0.0f;
-    if (m_new == -INFINITY) {
+    // move the reference only when needed (first finite logit, or > 2^kLazy growth)
+    float alpha = 1.0f;
+    if (cmax > m_ref + kLazy || (m_ref == -INFINITY && cmax != -INFINITY)) {
+      alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - cmax);
+      m_ref = cmax;
+    }
+    float p[8], psum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.0f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = exp2f(lg[i] - m_new);
-        psum += p[i];
-      }
+    for (int i = 0; i < 8; ++i) {
+      p[i] = m_ref == -INFINITY ? 0.0f : exp2f(lg[i] - m_ref);
+      psum += p[i];
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // rescale: this lane's O rows are heads 4g+i
-    float al[4];
+    if (__ballot(alpha != 1.0f)) {
+      float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
+      for (int n = 0; n < DH / 16; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
+        for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
+      }
     }
     // P (scaled by the key's value scale) as hi + lo bf16 A operands
     uint32_t hw[4], lw[4];
@@ -246,46 +298,51 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_attn_kernel(
     }
     const bf16x8_t ahi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
     const bf16x8_t alo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-    // ---- O += P·V, one 16-dim tile per step; V slots follow P's key order
+    // ---- O += P·V over this wave's dims; V slots follow P's key order
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
-      const uint16_t* vr = &Vt[(16 * n + col) * VSTR];
+    for (int n = 0; n < DH / 16; ++n) {
+      const uint16_t* vr = &Vt[(dim0 + 16 * n + col) * VSTR];
       const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
       const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
       const bf16x8_t bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
       o[n] = mfma16x16x32(ahi, bv, o[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < DH / 16; ++n) {
+      const uint16_t* vr = &Vt[(dim0 + 16 * n + col) * VSTR];
+      const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
+      const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
+      const bf16x8_t bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
       o[n] = mfma16x16x32(alo, bv, o[n]);
     }
   }
 
   // ---- epilogue
-  float lr[4], mr[4];
+  float lr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lr[i] = __shfl(l_run, 4 * g + i);
-    mr[i] = __shfl(m_run, 4 * g + i);
-  }
+  for (int i = 0; i < 4; ++i) lr[i] = __shfl(l_run, 4 * g + i);
   if (n_splits == 1) {
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
+    for (int n = 0; n < DH / 16; ++n) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const size_t h = (size_t)row * H_q + head0 + 4 * g + i;
-        out[h * D + 16 * n + col] = lr[i] > 0.0f ? o[n][i] / lr[i] : 0.0f;
+        out[h * D + dim0 + 16 * n + col] = lr[i] > 0.0f ? o[n][i] / lr[i] : 0.0f;
       }
     }
-    if (lse != nullptr && lane < 16)
+    if (lse != nullptr && lane < 16 && dim0 == 0)
       lse[(size_t)row * H_q + head0 + col] =
-          l_run > 0.0f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+          l_run > 0.0f ? (m_ref + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
   } else {
     const size_t base = ((size_t)row * n_splits + split) * H_q;
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
+    for (int n = 0; n < DH / 16; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part_o[(base + head0 + 4 * g + i) * D + 16 * n + col] = o[n][i];
+      for (int i = 0; i < 4; ++i)
+        part_o[(base + head0 + 4 * g + i) * D + dim0 + 16 * n + col] = o[n][i];
     }
-    if (lane < 16) {
-      part_ml[(base + head0 + col) * 2 + 0] = m_run;
+    if (lane < 16 && dim0 == 0) {
+      part_ml[(base + head0 + col) * 2 + 0] = m_ref;
       part_ml[(base + head0 + col) * 2 + 1] = l_run;
     }
   }
@@ -338,17 +395,18 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
   }
   const float sm_log2 = sm_scale * 1.4426950408889634f;
   dim3 grid(p.n_splits, rows, p.head_groups);
-#define CSA2_ATTN(D_, W_)                                                                          \
-  hipLaunchKernelGGL((sparse_attn_kernel<D_, W_>), grid, dim3(W_ * 64), 0, st, q, codes, scales, N, \
-                     sel, K, swa, swa_scale, S, swa_pos0, n_win, q_pos, Tq, H_q, sm_log2,           \
+  const int hg = p.waves / 2;
+#define CSA2_ATTN(D_, HG_)                                                                          \
+  hipLaunchKernelGGL((sparse_attn_kernel<D_, HG_>), grid, dim3(HG_ * 2 * 64), 0, st, q, codes, scales, \
+                     N, sel, K, swa, swa_scale, S, swa_pos0, n_win, q_pos, Tq, H_q, sm_log2,          \
                      p.chunks_per_split, p.n_splits, part_o, part_ml, out, lse)
   if (d == 512) {
-    if (p.waves == 4) CSA2_ATTN(512, 4);
-    else if (p.waves == 2) CSA2_ATTN(512, 2);
+    if (hg == 4) CSA2_ATTN(512, 4);
+    else if (hg == 2) CSA2_ATTN(512, 2);
     else CSA2_ATTN(512, 1);
   } else {
-    if (p.waves == 4) CSA2_ATTN(256, 4);
-    else if (p.waves == 2) CSA2_ATTN(256, 2);
+    if (hg == 4) CSA2_ATTN(256, 4);
+    else if (hg == 2) CSA2_ATTN(256, 2);
     else CSA2_ATTN(256, 1);
   }
 #undef CSA2_ATTN

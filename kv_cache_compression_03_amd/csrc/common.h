@@ -98,6 +98,28 @@ CSA2_DEV f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 
 CSA2_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// ---------------------------------------------------------------- hardware conversions
+// Both checked exhaustively against the definitions on gfx950: with a unit scale
+// the FP4 one yields the exact E2M1 values of the two nibbles of byte `sel` (low
+// nibble first) and the FP8 one the exact bf16 images of two E4M3 bytes (low or
+// high 16-bit half of the word).  (The FP4 path applies only the exponent of a
+// non-unit scale, so scales are multiplied separately.)
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+template <int SEL>
+CSA2_DEV f32x2_t fp4x2_to_f32(uint32_t w) { return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL); }
+
+template <bool HI>
+CSA2_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// high halves of two floats -> packed bf16 pair (exact when both are bf16 values)
+CSA2_DEV uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 CSA2_DEV float wave_max(float v) {

@@ -9,9 +9,9 @@
 // queries of h_i heads, rows past Tq are zero), B = 16 keys.  Each wave keeps
 // its queries in registers for its whole entry range and streams keys straight
 // from global memory into the B operand.  The reduction axis is permuted so
-// that lane (entry e, slot group g) reads d_i*2/4 contiguous bytes of key e;
-// the queries are loaded with the same permutation, so the dot products are
-// unchanged.  The ReLU / head-weight / head-sum epilogue runs on the MFMA
+// that in MFMA step s the four lane groups of entry e read 64 contiguous bytes
+// of key e (16 B each); the queries use the same permutation, so the dot
+// products are unchanged.  The ReLU / head-weight / head-sum epilogue runs on the MFMA
 // output: a lane holds 4 heads of one query for one entry, and one or two
 // cross-lane adds finish the head sum.
 #include "common.h"
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < Tq) v = qrow[g * KS + s];
+      if (t < Tq) v = qrow[s * 4 + g];
       qa[s] = as_bf16x8(v);
     }
   }
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
       if (live) {
         const uint4* kr = reinterpret_cast<const uint4*>(kb + (size_t)row * DI);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kv[u][s] = kr[g * KS + s];
+        for (int s = 0; s < KS; ++s) kv[u][s] = kr[s * 4 + g];
       }
     }
 #pragma unroll

@@ -11,8 +11,8 @@
 // score) << 32 | (0xFFFFFFFF - index): keys are unique, larger is better, and
 // the score ties break to the lower index.
 //
-// Rows with at most kTopkCap visible entries are sorted whole in LDS (one
-// 1024-thread workgroup per row, bitonic).  Longer rows (decode over 64K-1M
+// Rows with at most kTopkCap visible entries are selected whole in LDS (one
+// 1024-thread workgroup per row: radix select of the K-th key, then ranks).  Longer rows (decode over 64K-1M
 // entries, a handful of rows) first go through two wide passes:
 //   chunkmax: split the row into C >= K chunks and take each chunk's maximum;
 //   filter:   T = min of the chunk maxima.  Those C maxima are C distinct entries
@@ -100,85 +100,57 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restric
   if (n <= kTopkCap) return;
   const long long e0 = (long long)blockIdx.x * 256 * kFilterPerThread;
   if (e0 >= n) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int clen = n / K;
   const int C = (n + clen - 1) / clen;
   __shared__ float red[4];
+  __shared__ int wsum[4];
+  __shared__ int base;
   float mn = INFINITY;
-  for (int c = threadIdx.x; c < C; c += 256) mn = fminf(mn, cmax[(size_t)r * 2 * K + c]);
+  for (int c = tid; c < C; c += 256) mn = fminf(mn, cmax[(size_t)r * 2 * K + c]);
   mn = wave_min(mn);
   if (lane == 0) red[wave] = mn;
   __syncthreads();
   const uint32_t tk = mono_key(fminf(fminf(red[0], red[1]), fminf(red[2], red[3])));
   const float* row = scores + (size_t)r * N;
+  float sv[kFilterPerThread];
+  uint32_t take = 0;
+#pragma unroll
   for (int it = 0; it < kFilterPerThread; ++it) {
-    const long long e = e0 + it * 256 + threadIdx.x;
-    float s = 0.0f;
-    bool take = false;
-    if (e < n) {
-      s = row[e];
-      take = mono_key(s) >= tk;
-    }
-    const unsigned long long mask = __ballot(take);
-    if (mask) {
-      const int nt = __popcll(mask);
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&cnt[r], nt);
-      base = __shfl(base, 0);
-      const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
-      if (take && pos < kTopkCap) {
-        cscore[(size_t)r * kTopkCap + pos] = s;
-        cidx[(size_t)r * kTopkCap + pos] = (int)e;
+    const long long e = e0 + it * 256 + tid;
+    sv[it] = e < n ? row[e] : 0.0f;
+    take |= (e < n && mono_key(sv[it]) >= tk) ? (1u << it) : 0u;
+  }
+  // workgroup prefix of the per-thread candidate counts, then one atomic per workgroup
+  const int mine = __popc(take);
+  int x = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (tid == 0) base = atomicAdd(&cnt[r], wsum[0] + wsum[1] + wsum[2] + wsum[3]);
+  __syncthreads();
+  int pos = base + x - mine;
+  for (int w2 = 0; w2 < wave; ++w2) pos += wsum[w2];
+#pragma unroll
+  for (int it = 0; it < kFilterPerThread; ++it) {
+    if (take & (1u << it)) {
+      if (pos < kTopkCap) {
+        cscore[(size_t)r * kTopkCap + pos] = sv[it];
+        cidx[(size_t)r * kTopkCap + pos] = (int)(e0 + it * 256 + tid);
       }
+      ++pos;
     }
   }
 }
 
 // ---------------------------------------------------------------- per-row select
 
-// Bitonic sort of P (power of two) 64-bit keys in LDS, descending.
-CSA2_DEV void bitonic_desc_u64(unsigned long long* a, int P) {
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (P >> 1); i += kSelThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;  // this run ends up descending when up
-        const unsigned long long x = a[lo], y = a[hi];
-        if (up ? (x < y) : (x > y)) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
 
-// Bitonic sort of P (power of two) ints in LDS, ascending.
-CSA2_DEV void bitonic_asc_i32(int* a, int P) {
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (P >> 1); i += kSelThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int x = a[lo], y = a[hi];
-        if (up ? (x > y) : (x < y)) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
 
-CSA2_DEV int pow2_at_least(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
 
 // Exact selection over a whole row in global memory (rows whose candidate list
 // overflowed).  Radix select on the 32-bit score key finds the K-th score T;
@@ -249,54 +221,103 @@ CSA2_DEV void radix_select_row(const float* __restrict__ row, int n, int k, int*
   }
 }
 
+// The k-th largest of `total` unique 64-bit keys in LDS, by 8-bit digits from the top;
+// stops early once a digit's bucket is taken whole.  Returns T such that exactly k keys
+// are >= T.
+CSA2_DEV unsigned long long radix_kth_u64(const unsigned long long* keys, int total, int k,
+                                          uint32_t* hist, unsigned long long* bcast) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  unsigned long long prefix = 0ull, mask = 0ull;
+  int need = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < total; i += kSelThreads) {
+      const unsigned long long key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns buckets 4l..4l+3; find the bucket where the count from the top reaches need
+      uint32_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = hist[4 * lane + q];
+      const int c = (int)(h[0] + h[1] + h[2] + h[3]);
+      int suf = c;  // inclusive suffix over lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o);
+        if (lane + o < 64) suf += y;
+      }
+      int run = suf - c;  // keys in buckets above this lane's
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (run < need && run + (int)h[q] >= need) {
+          bcast[0] = (unsigned long long)(4 * lane + q);
+          bcast[1] = (unsigned long long)(need - run);
+          bcast[2] = (unsigned long long)h[q];
+        }
+        run += (int)h[q];
+      }
+    }
+    __syncthreads();
+    const unsigned long long dsel = bcast[0];
+    const int need2 = (int)bcast[1], bucket = (int)bcast[2];
+    __syncthreads();
+    prefix |= dsel << shift;
+    mask |= 255ull << shift;
+    need = need2;
+    if (bucket == need) break;  // the whole bucket is taken: keys >= prefix are exactly k
+  }
+  return prefix;
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int N, const int* __restrict__ valid_len,
     const int* __restrict__ cand_map, int K, int* __restrict__ out, const int* __restrict__ cnt,
     const float* __restrict__ cscore, const int* __restrict__ cidx) {
   extern __shared__ unsigned long long keys[];  // kTopkCap keys (64 KB)
+  __shared__ int chosen[2048];
+  __shared__ uint32_t hist[256];
+  __shared__ unsigned long long bcast[4];
   __shared__ int misc[32];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n = row_len(valid_len, r, N);
   const bool direct = n <= kTopkCap;
   const int total = direct ? n : cnt[r];
-  const int k = min(K, direct ? n : min(total, n));
+  const int k = min(K, n);
   const float* row = scores + (size_t)r * N;
-  int* sel;
-  if (!direct && total > kTopkCap) {
-    sel = reinterpret_cast<int*>(keys + 1024);
+  if (!direct && (total > kTopkCap || total < k)) {
+    int* sel = reinterpret_cast<int*>(keys + 1024);
     radix_select_row(row, n, k, sel, reinterpret_cast<uint32_t*>(keys), misc);
+    for (int i = tid; i < k; i += kSelThreads) chosen[i] = sel[i];
+    __syncthreads();
   } else {
-    const int P = pow2_at_least(total > 0 ? total : 1);
-    for (int i = tid; i < P; i += kSelThreads) {
-      unsigned long long key = 0ull;
-      if (i < total) {
-        const float s = direct ? row[i] : cscore[(size_t)r * kTopkCap + i];
-        const int idx = direct ? i : cidx[(size_t)r * kTopkCap + i];
-        key = make_key(s, idx);
-      }
-      keys[i] = key;
+    for (int i = tid; i < total; i += kSelThreads) {
+      const float s = direct ? row[i] : cscore[(size_t)r * kTopkCap + i];
+      const int idx = direct ? i : cidx[(size_t)r * kTopkCap + i];
+      keys[i] = make_key(s, idx);
+    }
+    if (tid == 0) misc[0] = 0;
+    __syncthreads();
+    const unsigned long long T = k > 0 ? radix_kth_u64(keys, total, k, hist, bcast) : ~0ull;
+    for (int i = tid; i < total; i += kSelThreads) {
+      const unsigned long long key = keys[i];
+      if (key >= T) chosen[atomicAdd(&misc[0], 1)] = key_index(key);
     }
     __syncthreads();
-    bitonic_desc_u64(keys, P);
-    // the chosen indices go to a region the first k keys do not occupy
-    sel = reinterpret_cast<int*>(keys + (P > 4096 ? 6144 : 4096));
-    int idx_tmp[2];
-    int cnt_tmp = 0;
-    for (int i = tid; i < k; i += kSelThreads) idx_tmp[cnt_tmp++] = key_index(keys[i]);
-    __syncthreads();
-    cnt_tmp = 0;
-    for (int i = tid; i < k; i += kSelThreads) sel[i] = idx_tmp[cnt_tmp++];
   }
-  __syncthreads();
-  const int Pk = pow2_at_least(k > 0 ? k : 1);
-  for (int i = k + tid; i < Pk; i += kSelThreads) sel[i] = 0x7FFFFFFF;
-  __syncthreads();
-  bitonic_asc_i32(sel, Pk);
+  // output in ascending index order: rank = number of chosen indices below
   int* orow = out + (size_t)r * K;
   for (int i = tid; i < K; i += kSelThreads) {
-    int v = -1;
-    if (i < k) v = cand_map ? cand_map[(size_t)r * N + sel[i]] : sel[i];
-    orow[i] = v;
+    if (i < k) {
+      const int v = chosen[i];
+      int rank = 0;
+      for (int j = 0; j < k; ++j) rank += chosen[j] < v ? 1 : 0;
+      orow[rank] = cand_map ? cand_map[(size_t)r * N + v] : v;
+    } else {
+      orow[i] = -1;
+    }
   }
 }
 
