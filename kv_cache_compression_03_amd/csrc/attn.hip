@@ -11,8 +11,13 @@
 // 200 flops per byte of keys, so both products run on MFMA (16x16x32 bf16):
 //   * a workgroup owns one query row, up to 64 heads and a contiguous range of
 //     32-key chunks (split-K over the keys); its waves are (16-head group) x
-//     (half of the output dims), so Q and O each take 64 registers per lane and
-//     two waves fit per SIMD;
+//     (half of the dims): a wave reduces QK over its half of the dims (the pair
+//     sums partial logits through LDS) and accumulates O for its half, so it
+//     holds 32 registers of Q and 64 of O, and two waves fit per SIMD;
+//   * workgroup ids are mapped XCD-aware: a row's splits and head groups share
+//     one XCD's L2;
+//   * LDS layouts and the lane-to-data mapping of the dequantisation keep bank
+//     conflicts at or below 2-way;
 //   * per chunk the workgroup dequantises the 32 keys once into LDS, exactly, as
 //     bf16 (E2M1 x E4M3 and E4M3 values fit bf16; hardware FP4/FP8 conversions),
 //     in two layouts: key-major for S^T = K·Q^T and dim-major for O += P·V; the
@@ -23,7 +28,8 @@
 //     reduction is permuted consistently in P and V);
 //   * P is split into bf16 hi + lo parts (two MFMAs), so P·V keeps ~16 bits of
 //     the fp32 probabilities; logits and sums stay in fp32;
-//   * online softmax in base 2 against a lazily moved reference maximum; per-split
+//   * online softmax in base 2 against a lazily moved reference maximum (no
+//     cross-lane traffic on the common path); per-split
 //     (O, m, l) partials are merged by a small combine kernel (or written
 //     directly when there is one split).
 #include "common.h"
@@ -32,6 +38,10 @@
 namespace csa2 {
 
 constexpr int kKC = 32;  // keys per chunk
+constexpr int kMaxSplits = 64;  // key splits a row may be cut into
+#ifndef CSA2_ATTN_TARGET_WGS
+#define CSA2_ATTN_TARGET_WGS 256  // workgroups a launch aims for (splits = target / rows)
+#endif
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -50,9 +60,10 @@ AttnPlan attn_plan(int B, int Tq, int H_q, int K, int L_max) {
   p.waves = hg * ds;
   p.head_groups = (H_q / 16) / hg;
   const long long base = (long long)B * Tq * p.head_groups;
-  const int max_chunks = (L_max + kKC - 1) / kKC + 1;  // +1: a chunk holds one kind of key
-  long long want = (256 + base - 1) / base;
+  const int max_chunks = (K + kKC - 1) / kKC + (L_max - K + kKC - 1) / kKC;  // selection, then window
+  long long want = (CSA2_ATTN_TARGET_WGS + base - 1) / base;
   int ns = (int)(want < 1 ? 1 : (want > max_chunks ? max_chunks : want));
+  if (ns > kMaxSplits) ns = kMaxSplits;
   p.chunks_per_split = (max_chunks + ns - 1) / ns;
   if (p.chunks_per_split < 1) p.chunks_per_split = 1;
   p.n_splits = (max_chunks + p.chunks_per_split - 1) / p.chunks_per_split;
@@ -67,6 +78,26 @@ size_t attn_ws_bytes(int B, int Tq, int H_q, int d, int K, int L_max) {
          align256(rows * p.n_splits * H_q * 2 * sizeof(float));
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by id, and each XCD has its
+// own L2.  With >= 8 rows, all workgroups of a row (its key splits and head
+// groups) are placed on one XCD, so the row's queries and partial results are
+// shared through that L2.  Returns false for the padding ids of the last round.
+CSA2_DEV bool xcd_map(int id, int rows, int per_row, int& row, int& unit) {
+  if (rows < 8) {
+    row = id / per_row;
+    unit = id - row * per_row;
+    return row < rows;
+  }
+  const int x = id & 7, k = id >> 3;
+  const int lr = k / per_row;
+  unit = k - lr * per_row;
+  row = lr * 8 + x;
+  return row < rows;
+}
+static inline int xcd_grid(int rows, int per_row) {
+  return rows < 8 ? rows * per_row : 8 * ((rows + 7) / 8) * per_row;
+}
+
 // Softmax state is kept against a reference maximum that only moves when a new
 // logit exceeds it by more than 2^kLazy (log2 units), so O is rarely rescaled;
 // probabilities stay below 2^kLazy, far inside float range.
@@ -78,38 +109,34 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
     const uint8_t* __restrict__ scales, int N, const int* __restrict__ sel, int K,
     const uint8_t* __restrict__ swa, float swa_scale, int S, long long swa_pos0, int n_win,
     const int* __restrict__ q_pos, int Tq, int H_q, float sm_log2, int chunks_per_split,
-    int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml,
-    float* __restrict__ out, float* __restrict__ lse) {
+    int n_splits, int rows, int head_groups, float* __restrict__ part_o,
+    float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int DS = 2;                       // output-dim halves
   constexpr int NT = HG * DS * 64;
   constexpr int DH = D / DS;                  // output dims per wave
   constexpr int KSTR = D + 8;                 // key-major row stride (bf16): 16 B pad
-  constexpr int VSTR = kKC + 4;               // dim-major row stride (bf16): 72 B
+  constexpr int VSTR = kKC + 8;               // dim-major row stride (bf16): 80 B
   constexpr int NB = (kKC / 4) * (D / 8);     // 4-key x 8-dim dequantisation blocks
   constexpr int ITER = (NB + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint16_t Krow[kKC * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
-  __shared__ int s_sel[2048];
+  __shared__ __attribute__((aligned(16))) float s_part[HG * 2 * 64 * 8];  // partial logits
   __shared__ float s_ksc[kKC];
   __shared__ int s_valid[kKC];
-  __shared__ int s_nsel;
 
-  const int split = blockIdx.x, row = blockIdx.y, hgrp = blockIdx.z;
+  int row, split, hgrp;
+  if (!xcd_map(blockIdx.x, rows, n_splits * head_groups, row, split)) return;
+  hgrp = split % head_groups;
+  split /= head_groups;
   const int b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
   const int head0 = (hgrp * HG + (wave % HG)) * 16;
   const int dim0 = (wave / HG) * DH;
 
+  // the selection occupies K slots (ascending, -1 padded); slots that are not a
+  // valid entry are masked, so no pass over the list is needed first
   const int* srow = sel + (size_t)row * K;
-  if (tid == 0) s_nsel = 0;
-  __syncthreads();
-  int cv = 0;
-  for (int i = tid; i < K; i += NT) cv += srow[i] >= 0 ? 1 : 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cv += __shfl_xor(cv, o);
-  if (lane == 0) atomicAdd(&s_nsel, cv);
-  __syncthreads();
-  const int n_sel = N > 0 ? s_nsel : 0;
+  const int n_sel = N > 0 ? K : 0;
 
   int swa_lo = 0, n_swa = S;
   if (q_pos != nullptr) {
@@ -125,11 +152,6 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
   const int n_chunks = nm + (n_swa + kKC - 1) / kKC;
   const int c_begin = split * chunks_per_split;
   const int c_end = min(n_chunks, c_begin + chunks_per_split);
-  const int sl_lo = c_begin * kKC;
-  const int sl_hi = min(min(c_end, nm) * kKC, n_sel);
-  for (int i = sl_lo + tid; i < sl_hi; i += NT) s_sel[i - sl_lo] = srow[i];
-  __syncthreads();
-
   // raw bytes of one chunk: per 4-key x 8-dim block, ra = 4 code bytes (or window
   // bytes 0-3), rb = the scale byte (or window bytes 4-7)
   uint32_t ra[ITER][4], rb[ITER][4];
@@ -139,12 +161,12 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
     for (int it = 0; it < ITER; ++it) {
       const int bid = tid + it * NT;
       if (bid < NB) {
-        const int kq = bid / (D / 8), dg = bid - kq * (D / 8);
+        const int kq = bid & 7, dg = bid >> 3;  // 8 key quads per lane octet: conflict-free LDS writes
         if (main) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int slot = c * kKC + 4 * kq + j;
-            int e = slot < n_sel ? s_sel[slot - sl_lo] : 0;
+            int e = slot < n_sel ? srow[slot] : 0;
             e = (e >= 0 && e < N) ? e : 0;
             const size_t ent = (size_t)b * N + e;
             ra[it][j] = *reinterpret_cast<const uint32_t*>(codes + ent * (D / 2) + 4 * dg);
@@ -164,11 +186,12 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
     }
   };
 
-  bf16x8_t qb[D / 32];
+  // this wave's half of the QK reduction: dims [dim0, dim0 + DH)
+  bf16x8_t qb[DH / 32];
   {
-    const uint4* qr = reinterpret_cast<const uint4*>(q + ((size_t)row * H_q + head0 + col) * D);
+    const uint4* qr = reinterpret_cast<const uint4*>(q + ((size_t)row * H_q + head0 + col) * D + dim0);
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qb[s] = as_bf16x8(qr[4 * s + g]);
+    for (int s = 0; s < DH / 32; ++s) qb[s] = as_bf16x8(qr[4 * s + g]);
   }
   f32x4_t o[DH / 16];
 #pragma unroll
@@ -183,7 +206,7 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
       bool valid;
       if (main) {
         const int slot = c * kKC + tid;
-        const int e = slot < n_sel ? s_sel[slot - sl_lo] : -1;
+        const int e = slot < n_sel ? srow[slot] : -1;
         valid = e >= 0 && e < N;
       } else {
         valid = (c - nm) * kKC + tid < n_swa;
@@ -196,7 +219,7 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
     for (int it = 0; it < ITER; ++it) {
       const int bid = tid + it * NT;
       if (bid < NB) {
-        const int kq = bid / (D / 8), dg = bid - kq * (D / 8);
+        const int kq = bid & 7, dg = bid >> 3;  // 8 key quads per lane octet: conflict-free LDS writes
         uint32_t v[4][4];  // [key][dim pair] packed bf16 pairs
         if (main) {
 #pragma unroll
@@ -237,13 +260,26 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
     if (c + 1 < c_end) load_chunk(c + 1);
 
     // ---- S^T = K·Q^T: rows = keys (two 16-key tiles), columns = this wave's heads
+    // each wave of a pair reduces over its half of the dims; the halves are summed
+    // through LDS (a + b == b + a, so both waves hold identical logits)
     f32x4_t st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&Krow[col * KSTR + 32 * s + 8 * g]);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(&Krow[(16 + col) * KSTR + 32 * s + 8 * g]);
+    for (int s = 0; s < DH / 32; ++s) {
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&Krow[col * KSTR + dim0 + 32 * s + 8 * g]);
+      const bf16x8_t a1 =
+          *reinterpret_cast<const bf16x8_t*>(&Krow[(16 + col) * KSTR + dim0 + 32 * s + 8 * g]);
       st0 = mfma16x16x32(a0, qb[s], st0);
       st1 = mfma16x16x32(a1, qb[s], st1);
+    }
+    {
+      float4* mine = reinterpret_cast<float4*>(&s_part[(wave * 64 + lane) * 8]);
+      mine[0] = make_float4(st0[0], st0[1], st0[2], st0[3]);
+      mine[1] = make_float4(st1[0], st1[1], st1[2], st1[3]);
+      __syncthreads();
+      const float4* other = reinterpret_cast<const float4*>(&s_part[(((wave + HG) % (2 * HG)) * 64 + lane) * 8]);
+      const float4 o0 = other[0], o1 = other[1];
+      st0[0] += o0.x; st0[1] += o0.y; st0[2] += o0.z; st0[3] += o0.w;
+      st1[0] += o1.x; st1[1] += o1.y; st1[2] += o1.z; st1[3] += o1.w;
     }
     // lane owns head `col`, keys 4g+i (tile 0) and 16+4g+i (tile 1)
     float lg[8], ks[8];
@@ -255,27 +291,22 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
       lg[i] = s_valid[k0] ? st0[i] * ks[i] * sm_log2 : -INFINITY;
       lg[4 + i] = s_valid[k1] ? st1[i] * ks[4 + i] * sm_log2 : -INFINITY;
     }
-    float cmax = lg[0];
+    // Lazy reference maximum: the four lane groups of a head only need to agree on
+    // it when one of them sees a logit more than 2^kLazy above it (the first chunk,
+    // or rarely later); then, and only then, the maximum is reduced across lanes.
+    float lmax = lg[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, lg[i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    // move the reference only when needed (first finite logit, or > 2^kLazy growth)
+    for (int i = 1; i < 8; ++i) lmax = fmaxf(lmax, lg[i]);
+    const bool grow = lmax > m_ref + kLazy || (m_ref == -INFINITY && lmax != -INFINITY);
     float alpha = 1.0f;
-    if (cmax > m_ref + kLazy || (m_ref == -INFINITY && cmax != -INFINITY)) {
-      alpha = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - cmax);
-      m_ref = cmax;
-    }
-    float p[8], psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = m_ref == -INFINITY ? 0.0f : exp2f(lg[i] - m_ref);
-      psum += p[i];
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {
+    if (__ballot(grow)) {
+      float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      if (cmax > m_ref + kLazy || (m_ref == -INFINITY && cmax != -INFINITY)) {
+        alpha = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - cmax);
+        m_ref = cmax;
+      }
+      l_run *= alpha;
       float al[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
@@ -285,39 +316,48 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
         for (int i = 0; i < 4; ++i) o[n][i] *= al[i];
       }
     }
-    // P (scaled by the key's value scale) as hi + lo bf16 A operands
+    // probabilities (this lane's share of the row sum is kept per lane)
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i] - m_ref);
+      l_run += p[i];
+    }
+    // P (scaled by the key's value scale) as hi + lo bf16 A operands: hi keeps the
+    // top 8 significant bits, lo the next 8 of the exact remainder
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const float x0 = p[2 * jj] * ks[2 * jj], x1 = p[2 * jj + 1] * ks[2 * jj + 1];
-      const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
-      const uint32_t l0 = f32_to_bf16_rne(x0 - bf16_to_f32(h0));
-      const uint32_t l1 = f32_to_bf16_rne(x1 - bf16_to_f32(h1));
-      hw[jj] = h0 | (h1 << 16);
-      lw[jj] = l0 | (l1 << 16);
+      const float h0 = __uint_as_float(__float_as_uint(x0) & 0xFFFF0000u);
+      const float h1 = __uint_as_float(__float_as_uint(x1) & 0xFFFF0000u);
+      hw[jj] = pack_hi16(h0, h1);
+      lw[jj] = pack_hi16(x0 - h0, x1 - h1);
     }
     const bf16x8_t ahi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
     const bf16x8_t alo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-    // ---- O += P·V over this wave's dims; V slots follow P's key order
+    // ---- O += P·V over this wave's dims; V slots follow P's key order.  Each V
+    // fragment is read once and used by the hi and the lo MFMA.
 #pragma unroll
-    for (int n = 0; n < DH / 16; ++n) {
-      const uint16_t* vr = &Vt[(dim0 + 16 * n + col) * VSTR];
-      const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
-      const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-      const bf16x8_t bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-      o[n] = mfma16x16x32(ahi, bv, o[n]);
-    }
+    for (int n0 = 0; n0 < DH / 16; n0 += 4) {
+      bf16x8_t bv[4];
 #pragma unroll
-    for (int n = 0; n < DH / 16; ++n) {
-      const uint16_t* vr = &Vt[(dim0 + 16 * n + col) * VSTR];
-      const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
-      const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-      const bf16x8_t bv = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-      o[n] = mfma16x16x32(alo, bv, o[n]);
+      for (int u = 0; u < 4; ++u) {
+        const uint16_t* vr = &Vt[(dim0 + 16 * (n0 + u) + col) * VSTR];
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
+        bv[u] = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[n0 + u] = mfma16x16x32(ahi, bv[u], o[n0 + u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[n0 + u] = mfma16x16x32(alo, bv[u], o[n0 + u]);
     }
   }
 
-  // ---- epilogue
+  // ---- epilogue: row sums were kept per lane group
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
   float lr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lr[i] = __shfl(l_run, 4 * g + i);
@@ -350,30 +390,51 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
 
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
-                                                           int n_splits, int H_q, int D,
+                                                           int n_splits, int H_q, int D, int rows,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
-  const int row = blockIdx.x, h = blockIdx.y;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    M = fmaxf(M, part_ml[(((size_t)row * n_splits + s) * H_q + h) * 2]);
-  float wsum = 0.0f;
-  for (int s = 0; s < n_splits; ++s) {
-    const size_t ix = (((size_t)row * n_splits + s) * H_q + h) * 2;
-    const float ms = part_ml[ix];
-    if (ms != -INFINITY) wsum += part_ml[ix + 1] * exp2f(ms - M);
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[2];
+  int row, h;
+  if (!xcd_map(blockIdx.x, rows, H_q, row, h)) return;
+  const int tid = threadIdx.x;
+  const size_t base = (size_t)row * n_splits * H_q + h;  // split s of this head: base + s*H_q
+  float ms = -INFINITY, ls = 0.0f;
+  if (tid < n_splits) {
+    ms = part_ml[(base + (size_t)tid * H_q) * 2];
+    ls = part_ml[(base + (size_t)tid * H_q) * 2 + 1];
   }
+  float M = ms;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (tid < 64 && (tid & 63) == 0) red[0] = M;
+  __syncthreads();
+  M = red[0];
+  const float e = (tid < n_splits && ms != -INFINITY) ? exp2f(ms - M) : 0.0f;
+  float wsum = ls * e;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+  if (tid == 0) red[1] = wsum;
+  if (tid < n_splits) wgt[tid] = e;
+  __syncthreads();
+  wsum = red[1];
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  for (int dd = threadIdx.x; dd < D; dd += 128) {
-    float acc = 0.0f;
+  for (int d4 = tid; d4 < D / 4; d4 += 128) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < n_splits; ++s) {
-      const size_t ix = ((size_t)row * n_splits + s) * H_q + h;
-      const float ms = part_ml[ix * 2];
-      if (ms != -INFINITY) acc += part_o[ix * D + dd] * exp2f(ms - M);
+      const float ws = wgt[s];
+      if (ws != 0.0f) {
+        const float4 v = reinterpret_cast<const float4*>(part_o + (base + (size_t)s * H_q) * D)[d4];
+        acc.x += v.x * ws;
+        acc.y += v.y * ws;
+        acc.z += v.z * ws;
+        acc.w += v.w * ws;
+      }
     }
-    out[((size_t)row * H_q + h) * D + dd] = acc * inv;
+    reinterpret_cast<float4*>(out + ((size_t)row * H_q + h) * D)[d4] =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
-  if (lse != nullptr && threadIdx.x == 0)
+  if (lse != nullptr && tid == 0)
     lse[(size_t)row * H_q + h] = wsum > 0.0f ? (M + log2f(wsum)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -394,12 +455,12 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
                                        align256((size_t)rows * p.n_splits * H_q * d * sizeof(float)));
   }
   const float sm_log2 = sm_scale * 1.4426950408889634f;
-  dim3 grid(p.n_splits, rows, p.head_groups);
+  dim3 grid(xcd_grid(rows, p.n_splits * p.head_groups));
   const int hg = p.waves / 2;
 #define CSA2_ATTN(D_, HG_)                                                                          \
   hipLaunchKernelGGL((sparse_attn_kernel<D_, HG_>), grid, dim3(HG_ * 2 * 64), 0, st, q, codes, scales, \
                      N, sel, K, swa, swa_scale, S, swa_pos0, n_win, q_pos, Tq, H_q, sm_log2,          \
-                     p.chunks_per_split, p.n_splits, part_o, part_ml, out, lse)
+                     p.chunks_per_split, p.n_splits, rows, p.head_groups, part_o, part_ml, out, lse)
   if (d == 512) {
     if (hg == 4) CSA2_ATTN(512, 4);
     else if (hg == 2) CSA2_ATTN(512, 2);
@@ -411,8 +472,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
   }
 #undef CSA2_ATTN
   if (p.n_splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(rows, H_q), dim3(128), 0, st, part_o, part_ml,
-                       p.n_splits, H_q, d, out, lse);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, H_q)), dim3(128), 0, st, part_o,
+                       part_ml, p.n_splits, H_q, d, rows, out, lse);
   return hipGetLastError();
 }
 

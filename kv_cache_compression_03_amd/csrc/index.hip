@@ -20,7 +20,13 @@
 namespace csa2 {
 
 constexpr int kScanWaves = 4;
-constexpr int kScanBatch = 4;  // entry tiles whose keys are in flight together
+#ifndef CSA2_SCAN_BATCH
+#define CSA2_SCAN_BATCH 2
+#endif
+#ifndef CSA2_SCAN_TARGET_WGS
+#define CSA2_SCAN_TARGET_WGS 16384
+#endif
+constexpr int kScanBatch = CSA2_SCAN_BATCH;  // entry tiles whose keys are in flight together
 
 template <int HI, int DI>
 __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
@@ -117,8 +123,9 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   const int qpt = 16 / h_i;
   const int qgroups = (Tq + qpt - 1) / qpt;
   const long long tiles = ((long long)L + 15) / 16;
-  // aim for >= 2048 workgroups in total, at most 32 tiles (512 entries) per wave
-  long long per_wave = ((long long)tiles * B * qgroups + 2048LL * kScanWaves - 1) / (2048LL * kScanWaves);
+  // aim for about CSA2_SCAN_TARGET_WGS workgroups, at most 32 tiles (512 entries) per wave
+  const long long target = CSA2_SCAN_TARGET_WGS;
+  long long per_wave = ((long long)tiles * B * qgroups + target * kScanWaves - 1) / (target * kScanWaves);
   int tpw = (int)(per_wave < 1 ? 1 : (per_wave > 32 ? 32 : per_wave));
   tpw = (tpw + kScanBatch - 1) / kScanBatch * kScanBatch;
   const long long bx = (tiles + (long long)tpw * kScanWaves - 1) / ((long long)tpw * kScanWaves);
