@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size reference "
+                         "for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -174,6 +177,15 @@ def main():
         raise SystemExit("workloads built from hidden states are parity cases, not bench lines")
     log(f"workload {wl.name}: B={wl.B} N={wl.N} d={wl.d} schedule={wl.schedule}")
     codes, scales, kidx, layers = build_inputs(wl, torch, bd, sch)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
     run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
                              G=wl.G, PB=wl.PB, PE=wl.PE)
     if args.no_graph:
@@ -204,12 +216,17 @@ def main():
     log(f"scan kernel: {scan_s * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
 
     traffic = None
-    tf = os.path.join(ROOT, "profiles", f"traffic_index_scores_{wl.name}.json")
+    tf = os.path.join(ROOT, "profiles", f"traffic_index_scores_{wl.name}.txt")
     if os.path.exists(tf):
+        rec = {}
         with open(tf) as f:
-            rec = json.load(f)
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split("=", 1)
+                    rec[k.strip()] = v.strip()
+        # counters taken on an older kernel source no longer describe this one
         if rec.get("source_sha") == source_sha("index.hip", "common.h"):
-            traffic = rec.get("hbm_bytes_per_launch")
+            traffic = int(rec["hbm_bytes_per_launch"])
 
     out = {
         "metric": METRIC,
