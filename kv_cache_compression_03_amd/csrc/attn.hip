@@ -39,6 +39,7 @@ namespace csa2 {
 
 constexpr int kKC = 32;  // keys per chunk
 constexpr int kMaxSplits = 64;  // key splits a row may be cut into
+constexpr int kMaxSel = 2048;   // selection slots a row may hold (all staged in LDS)
 #ifndef CSA2_ATTN_TARGET_WGS
 #define CSA2_ATTN_TARGET_WGS 256  // workgroups a launch aims for (splits = target / rows)
 #endif
@@ -121,6 +122,7 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Krow[kKC * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
   __shared__ __attribute__((aligned(16))) float s_part[HG * 2 * 64 * 8];  // partial logits
+  __shared__ int s_ent[kMaxSel];  // entry of each selection slot this split reads
   __shared__ float s_ksc[kKC];
   __shared__ int s_valid[kKC];
 
@@ -152,6 +154,13 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
   const int n_chunks = nm + (n_swa + kKC - 1) / kKC;
   const int c_begin = split * chunks_per_split;
   const int c_end = min(n_chunks, c_begin + chunks_per_split);
+  // the entries of this split's selection slots, staged once (invalid -> entry 0)
+  const int sl_lo = c_begin * kKC, sl_hi = min(c_end, nm) * kKC;
+  for (int i = sl_lo + tid; i < sl_hi; i += NT) {
+    const int v = i < n_sel ? srow[i] : -1;
+    s_ent[i - sl_lo] = (v >= 0 && v < N) ? v : -1;
+  }
+  __syncthreads();
   // raw bytes of one chunk: per 4-key x 8-dim block, ra = 4 code bytes (or window
   // bytes 0-3), rb = the scale byte (or window bytes 4-7)
   uint32_t ra[ITER][4], rb[ITER][4];
@@ -165,9 +174,7 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
         if (main) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int slot = c * kKC + 4 * kq + j;
-            int e = slot < n_sel ? srow[slot] : 0;
-            e = (e >= 0 && e < N) ? e : 0;
+            const int e = max(s_ent[c * kKC + 4 * kq + j - sl_lo], 0);
             const size_t ent = (size_t)b * N + e;
             ra[it][j] = *reinterpret_cast<const uint32_t*>(codes + ent * (D / 2) + 4 * dg);
             rb[it][j] = scales[ent * (D / 16) + (dg >> 1)];
@@ -192,6 +199,11 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
     const uint4* qr = reinterpret_cast<const uint4*>(q + ((size_t)row * H_q + head0 + col) * D + dim0);
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s) qb[s] = as_bf16x8(qr[4 * s + g]);
+    // Wait for the query here, once.  Otherwise the wait for it is placed inside
+    // the chunk loop (the compiler cannot prove it done on loop entry), and since
+    // loads retire in order that wait also drains the next chunk's prefetch.
+#pragma unroll
+    for (int s = 0; s < DH / 32; ++s) asm volatile("" : "+v"(qb[s]));
   }
   f32x4_t o[DH / 16];
 #pragma unroll
@@ -201,13 +213,11 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
   if (c_begin < c_end) load_chunk(c_begin);
   for (int c = c_begin; c < c_end; ++c) {
     const bool main = c < nm;
-    __syncthreads();  // the previous chunk's LDS reads are done
+    lds_barrier();  // the previous chunk's LDS reads are done
     if (tid < kKC) {
       bool valid;
       if (main) {
-        const int slot = c * kKC + tid;
-        const int e = slot < n_sel ? srow[slot] : -1;
-        valid = e >= 0 && e < N;
+        valid = s_ent[c * kKC + tid - sl_lo] >= 0;
       } else {
         valid = (c - nm) * kKC + tid < n_swa;
       }
@@ -255,7 +265,7 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // the next chunk's loads fly while this chunk is multiplied
     if (c + 1 < c_end) load_chunk(c + 1);
 
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
       float4* mine = reinterpret_cast<float4*>(&s_part[(wave * 64 + lane) * 8]);
       mine[0] = make_float4(st0[0], st0[1], st0[2], st0[3]);
       mine[1] = make_float4(st1[0], st1[1], st1[2], st1[3]);
-      __syncthreads();
+      lds_barrier();
       const float4* other = reinterpret_cast<const float4*>(&s_part[(((wave + HG) % (2 * HG)) * 64 + lane) * 8]);
       const float4 o0 = other[0], o1 = other[1];
       st0[0] += o0.x; st0[1] += o0.y; st0[2] += o0.z; st0[3] += o0.w;

@@ -120,6 +120,15 @@ CSA2_DEV uint32_t pack_hi16(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
+// ---------------------------------------------------------------- barriers
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() is a workgroup fence
+// plus s_barrier, and the fence makes every wave wait for all of its outstanding
+// global loads first, which would serialise prefetches issued before the
+// barrier.  Here only LDS operations are drained (lgkmcnt); loads in flight keep
+// flying and the compiler still waits for their registers before first use.
+CSA2_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- wave reductions
 
 CSA2_DEV float wave_max(float v) {
