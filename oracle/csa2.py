@@ -439,6 +439,77 @@ def decode_step(schedule: Sequence[str], layers: Sequence[LayerInputs], codes, s
     return res
 
 
+@dataclass
+class PrefillLayerInputs:
+    q_main: np.ndarray                  # [Tq, H_q, d] bf16 bits
+    swa: np.ndarray                     # [S, d] E4M3 codes; row i is position swa_pos0 + i
+    q_idx: Optional[np.ndarray] = None  # [Tq, h_i, d_i] bf16 bits (Full layers)
+    w: Optional[np.ndarray] = None      # [Tq, h_i]
+
+
+@dataclass
+class PrefillResult:
+    kv: np.ndarray                      # [n_new, d] float64: the chunk's compressed entries
+    entries: FP4Entries                 # their FP4 form
+    k_new: np.ndarray                   # [n_new, d_i] bf16 bits: their indexer keys
+    rows: np.ndarray                    # query rows evaluated
+    sel: List[np.ndarray] = field(default_factory=list)   # per layer [len(rows), K]
+    out: List[np.ndarray] = field(default_factory=list)   # per layer [len(rows), H_q, d]
+
+
+def prefill_chunk(schedule: Sequence[str], layers: Sequence[PrefillLayerInputs], H, W_kv, W_z,
+                  m: int, pos0: int, codes_pre, scales_pre, k_pre, W_ik, K: int = 512,
+                  swa_pos0: int = 0, n_win: int = 128, swa_scale: float = 1.0,
+                  rows: Optional[Sequence[int]] = None, rope_dim: int = 64,
+                  sm_scale: Optional[float] = None) -> PrefillResult:
+    """One prefill chunk through an encoder layer schedule.
+
+    [deep-dive §3.1, §3.2] the chunk's hidden states (tokens pos0 .. pos0+Tq-1)
+    are compressed into new entries, which are quantised and given indexer keys
+    and appended after the entries already cached (codes_pre etc., entry j at
+    position (j+1)m-1, so pos0 must be a multiple of m).  Every chunk token is
+    then a query at its own position t: a Full layer scores the entries visible
+    to it (R3/R15: p_j <= t) and takes their Top-K; Reuse layers keep that
+    selection (R12); SWA-only layers attend to the window alone; every layer
+    attends over the selection and the window [t - n_win + 1, t] (R14).
+    ``rows`` limits the evaluation to some query rows (all when None).
+    """
+    if pos0 % m:
+        raise ValueError("pos0 must be a multiple of m")
+    kv = compress(H, W_kv, W_z, m, pos0, rope_dim)
+    q8 = quant_fp4(kv.astype(np.float32))  # the entries are stored as float32, then quantised
+    k_new = indexer_k(q8.codes, q8.scales, W_ik)
+    codes = np.concatenate([np.asarray(codes_pre), q8.codes], axis=0)
+    scales = np.concatenate([np.asarray(scales_pre), q8.scales], axis=0)
+    k_all = np.concatenate([np.asarray(k_pre), k_new], axis=0)
+    n = codes.shape[0]
+    Tq = np.asarray(H).shape[0]
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    res = PrefillResult(kv=kv, entries=q8, k_new=k_new, rows=rows)
+    empty = np.full(K, -1, dtype=np.int64)
+    sel = [None] * len(rows)
+    for mode, li in zip(schedule, layers):
+        if mode not in (FULL, REUSE, SWA_ONLY):
+            raise ValueError(f"prefill layer mode {mode!r}")
+        S_l, O_l = [], []
+        for r, t in enumerate(rows):
+            pos = pos0 + int(t)
+            if mode == FULL:
+                nvis = visible_count(pos, n, m)
+                s = index_scores(li.q_idx[t], li.w[t], k_all[:nvis])
+                sel[r] = topk(s, K, nvis)
+            elif mode == REUSE and sel[r] is None:
+                raise ValueError("Reuse before any Full layer")
+            cur = empty if mode == SWA_ONLY else sel[r]
+            S_l.append(cur.copy())
+            O_l.append(sparse_attention(li.q_main[t], codes, scales, cur, li.swa, swa_scale,
+                                        q_pos=pos, swa_pos0=swa_pos0, n_win=n_win,
+                                        sm_scale=sm_scale))
+        res.sel.append(np.stack(S_l) if S_l else np.zeros((0, K), dtype=np.int64))
+        res.out.append(np.stack(O_l) if O_l else np.zeros((0,) + np.asarray(li.q_main).shape[1:]))
+    return res
+
+
 # --------------------------------------------------------------------------
 
 

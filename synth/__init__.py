@@ -57,6 +57,26 @@ class Workload:
     d_model: int = 0
     h_dtype: str = "f32"   # "f32" or "bf16"
     rope_dim: int = 64
+    # prefill: the last `chunk` of T tokens are the queries; the entries of the
+    # tokens before them are drawn directly (like decode KV), the chunk's own
+    # entries come from its hidden states through the compressor
+    chunk: int = 0
+    n_win: int = 128
+
+    @property
+    def pos0(self) -> int:
+        """Position of the first chunk token (prefill)."""
+        return self.T - self.chunk
+
+    @property
+    def n_pre(self) -> int:
+        """Entries that exist before the chunk (prefill)."""
+        return self.pos0 // self.m
+
+    @property
+    def swa_pos0(self) -> int:
+        """Position of the first window token a chunk query can see (prefill)."""
+        return max(0, self.pos0 - (self.n_win - 1))
 
     @property
     def layers(self) -> List[str]:
@@ -80,6 +100,11 @@ WORKLOADS = {
     # batch 8 x 1M, the 20-layer decoder schedule, 0.5% planted
     "decode_1m_b8": Workload("decode_1m_b8", B=8, N=1 << 20, d=512, h_i=8, d_i=128, H_q=64,
                              schedule="FUUURUUURUUURUUURUUU", seed=4, plant_frac=0.005),
+    # prefill chunk: the last 8,192 tokens of a 32,768-token sequence, m = 2
+    # (16,384 entries, 12,288 before the chunk), d_model 5,120 bf16, Full + 5 Reuse
+    "prefill_32k": Workload("prefill_32k", B=1, N=16384, d=512, h_i=8, d_i=128, H_q=64,
+                            S=8192 + 127, m=2, schedule="FUUUUU", seed=3, T=32768,
+                            chunk=8192, d_model=5120, h_dtype="bf16"),
 }
 
 
@@ -160,26 +185,48 @@ def main_kv(wl: Workload, b: int, lo: int = 0, hi: Optional[int] = None) -> np.n
     return x
 
 
-def q_index(wl: Workload, layer: int, b: int, Tq: int = 1) -> np.ndarray:
-    """Indexer query [Tq, h_i, d_i] bf16 bits."""
-    r = _rng(wl.seed, "qidx", layer, b)
-    q = r.standard_normal((Tq, wl.h_i, wl.d_i), dtype=np.float32)
+Q_CHUNK = 256  # query rows per random stream
+
+
+def _query_rows(wl: Workload, tag: str, layer: int, b: int, Tq: int, t0: int, shape, draw):
+    """Rows t0 .. t0+Tq-1 of a per-query tensor; row t comes from the stream of
+    query chunk t // Q_CHUNK, so any query range can be regenerated alone."""
+    out = np.empty((Tq,) + tuple(shape), dtype=np.float32)
+    t1 = t0 + Tq
+    for c in range(t0 // Q_CHUNK, -(-t1 // Q_CHUNK)):
+        c0 = c * Q_CHUNK
+        a, z = max(t0, c0), min(t1, c0 + Q_CHUNK)
+        blk = draw(_rng(wl.seed, tag, layer, b, c), (z - c0,) + tuple(shape))
+        out[a - t0:z - t0] = blk[a - c0:]
+    return out
+
+
+def q_index(wl: Workload, layer: int, b: int, Tq: int = 1, t0: int = 0) -> np.ndarray:
+    """Indexer query [Tq, h_i, d_i] bf16 bits (query rows t0 .. t0+Tq-1)."""
+    q = _query_rows(wl, "qidx", layer, b, Tq, t0, (wl.h_i, wl.d_i),
+                    lambda r, sh: r.standard_normal(sh, dtype=np.float32))
     if wl.plant_frac > 0:
         _, u = plant_direction(wl)
         q = q + (wl.alpha * u).astype(np.float32)[None, None, :]
     return to_bf16_bits(q)
 
 
-def head_weights(wl: Workload, layer: int, b: int, Tq: int = 1) -> np.ndarray:
+def head_weights(wl: Workload, layer: int, b: int, Tq: int = 1, t0: int = 0) -> np.ndarray:
     if wl.equal_w:
         return np.ones((Tq, wl.h_i), dtype=np.float32)
-    r = _rng(wl.seed, "w", layer, b)
-    return r.random((Tq, wl.h_i), dtype=np.float32)
+    return _query_rows(wl, "w", layer, b, Tq, t0, (wl.h_i,),
+                       lambda r, sh: r.random(sh, dtype=np.float32))
 
 
-def q_main(wl: Workload, layer: int, b: int, Tq: int = 1) -> np.ndarray:
-    r = _rng(wl.seed, "qmain", layer, b)
-    return to_bf16_bits(r.standard_normal((Tq, wl.H_q, wl.d), dtype=np.float32))
+def q_main(wl: Workload, layer: int, b: int, Tq: int = 1, t0: int = 0) -> np.ndarray:
+    """Main query [Tq, H_q, d] bf16 bits (query rows t0 .. t0+Tq-1)."""
+    return to_bf16_bits(_query_rows(wl, "qmain", layer, b, Tq, t0, (wl.H_q, wl.d),
+                                    lambda r, sh: r.standard_normal(sh, dtype=np.float32)))
+
+
+def q_positions(wl: Workload) -> np.ndarray:
+    """Positions of the chunk's queries (prefill): pos0 .. T-1, int32."""
+    return np.arange(wl.pos0, wl.T, dtype=np.int32)
 
 
 def swa_tokens(wl: Workload, layer: int, b: int, S: Optional[int] = None) -> np.ndarray:
@@ -188,9 +235,11 @@ def swa_tokens(wl: Workload, layer: int, b: int, S: Optional[int] = None) -> np.
 
 
 def hidden(wl: Workload, b: int = 0) -> np.ndarray:
-    """Hidden states [T, d_model]: float32, or bf16 bits when h_dtype == 'bf16'."""
+    """Hidden states of the tokens that go through the compressor: all T tokens,
+    or the chunk's tokens in prefill.  [T or chunk, d_model] float32, or bf16
+    bits when h_dtype == 'bf16'."""
     r = _rng(wl.seed, "H", 0, b)
-    h = r.standard_normal((wl.T, wl.d_model), dtype=np.float32)
+    h = r.standard_normal((wl.chunk or wl.T, wl.d_model), dtype=np.float32)
     return to_bf16_bits(h) if wl.h_dtype == "bf16" else h
 
 
