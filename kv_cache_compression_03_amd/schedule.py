@@ -1,4 +1,5 @@
-"""Decode step of a Full / Reindex / Reuse layer schedule on the CSA2 library.
+"""Decode step and prefill chunk of a Full / Reindex / Reuse layer schedule on the
+CSA2 library.
 
 [deep-dive §3.2] every attention layer is statically Full (fresh indexer scores
 and Top-K; the first Full layer of a step also builds the shared candidate pool,
@@ -110,3 +111,79 @@ class DecodeSchedule:
         with torch.cuda.graph(g):
             self.step(codes, scales, k_idx, layers)
         return g
+
+
+class PrefillChunk:
+    """One prefill chunk of one sequence through an encoder schedule.
+
+    [deep-dive §3.1, §3.2] the chunk's hidden states (tokens pos0 .. pos0+Tq-1)
+    are compressed into Tq/m new entries, which are quantised to FP4 with their
+    indexer keys and written after the n_pre entries already cached.  Every
+    chunk token is then a query at its own position: a Full layer scores the
+    entries visible to it (p_j <= t) and keeps its Top-K, Reuse layers keep that
+    selection, SWA-only layers attend to the window alone, and every layer
+    attends over the selection and the window [t - n_win + 1, t].
+
+    The cache (codes [1, N, d/2], scales [1, N, d/16], k_idx [1, N, d_i]) is the
+    caller's; this object owns the per-chunk buffers, allocated once.
+    """
+
+    def __init__(self, schedule: Sequence[str], N: int, n_pre: int, Tq: int, d: int, h_i: int,
+                 d_i: int, H_q: int, S: int, K: int = 512, m: int = 2, pos0: int = 0,
+                 swa_pos0: int = 0, n_win: int = 128, rope_dim: int = 64,
+                 swa_scale: float = 1.0, device: str = "cuda"):
+        self.layers: List[str] = list(schedule)
+        for i, mode in enumerate(self.layers):
+            if mode not in (FULL, REUSE, SWA_ONLY):
+                raise ValueError(f"layer {i}: prefill layers are Full, Reuse or SWA-only, got {mode!r}")
+            if mode == REUSE and FULL not in self.layers[:i]:
+                raise ValueError(f"layer {i}: Reuse before any Full layer")
+        if Tq % m or pos0 % m or n_pre != pos0 // m or n_pre + Tq // m > N:
+            raise ValueError("chunk geometry: need Tq and pos0 multiples of m, n_pre = pos0/m, "
+                             "n_pre + Tq/m <= N")
+        self.N, self.n_pre, self.Tq, self.d, self.h_i, self.d_i = N, n_pre, Tq, d, h_i, d_i
+        self.H_q, self.S, self.K, self.m, self.pos0 = H_q, S, K, m, pos0
+        self.swa_pos0, self.n_win, self.rope_dim, self.swa_scale = swa_pos0, n_win, rope_dim, swa_scale
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.n_new = Tq // m
+        self.kv_new = torch.empty(1, self.n_new, d, dtype=torch.float32, device=dev)
+        self.q_pos = torch.arange(pos0, pos0 + Tq, **i32).view(1, Tq)
+        # entries visible to each query: floor((t + 1) / m), at most N
+        self.valid_len = torch.clamp((self.q_pos.view(Tq) + 1) // m, max=N).to(torch.int32)
+        self.scores = torch.empty(1, Tq, N, dtype=torch.float32, device=dev)
+        self.sel: Dict[int, torch.Tensor] = {i: torch.empty(1, Tq, K, **i32)
+                                             for i, mo in enumerate(self.layers) if mo == FULL}
+        self.no_sel = torch.full((1, Tq, K), -1, **i32)
+        self.out = [torch.empty(1, Tq, H_q, d, dtype=torch.float32, device=dev) for _ in self.layers]
+        ws = max(bd.csa2_topk_workspace(Tq, N, K), bd.csa2_sparse_attn_workspace(1, Tq, H_q, d, K, S))
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+
+    def selection_of(self, layer: int) -> torch.Tensor:
+        if self.layers[layer] == SWA_ONLY:
+            return self.no_sel
+        for j in range(layer, -1, -1):
+            if j in self.sel:
+                return self.sel[j]
+        raise ValueError("no selection")
+
+    def step(self, H: torch.Tensor, W_kv: torch.Tensor, W_z: torch.Tensor, W_ik: torch.Tensor,
+             codes: torch.Tensor, scales: torch.Tensor, k_idx: torch.Tensor,
+             layers: Sequence[LayerBuffers], stream=None) -> List[torch.Tensor]:
+        """H [Tq, d_model] (bf16 or f32); layers[i]: q_main [1, Tq, H_q, d], swa [1, S, d] and,
+        for Full layers, q_idx [1, Tq, h_i, d_i], w [1, Tq, h_i].  Returns per-layer outputs."""
+        lo, hi = self.n_pre, self.n_pre + self.n_new
+        bd.csa2_compress(H.view(1, self.Tq, -1), W_kv, W_z, self.m, pos0=self.pos0,
+                         rope_dim=self.rope_dim, out=self.kv_new, stream=stream)
+        bd.csa2_quant_fp4(self.kv_new[0], codes=codes[0, lo:hi], scales=scales[0, lo:hi], W_ik=W_ik,
+                          k_idx=k_idx[0, lo:hi], stream=stream)
+        for i, (mode, lb) in enumerate(zip(self.layers, layers)):
+            if mode == FULL:
+                bd.csa2_index_full(lb.q_idx, lb.w, k_idx, q_pos=self.q_pos, m=self.m,
+                                   scores=self.scores, stream=stream)
+                bd.csa2_topk(self.scores.view(self.Tq, self.N), self.K, valid_len=self.valid_len,
+                             out=self.sel[i].view(self.Tq, self.K), ws=self.ws, stream=stream)
+            bd.csa2_sparse_attn(lb.q_main, codes, scales, self.selection_of(i), lb.swa,
+                                swa_scale=self.swa_scale, q_pos=self.q_pos, swa_pos0=self.swa_pos0,
+                                n_win=self.n_win, out=self.out[i], ws=self.ws, stream=stream)
+        return self.out

@@ -2,6 +2,7 @@
 import numpy as np
 import torch
 
+from oracle.codecs import bf16_to_f64
 from oracle.csa2 import topk as oracle_topk
 
 
@@ -42,3 +43,15 @@ def check_topk(gpu_sel, ref_scores, K, n_vis=None, rel=1e-4, index_map=None):
             jj = pos[j] if pos is not None else j
             assert abs(s[jj] - kth) <= tol, f"index {j}: score {s[jj]} vs K-th {kth}"
     return len(diff)
+
+
+def score_tol(q, w, k):
+    """fp32-accumulation bound of indexer scores: 2^-20 x sum_h w_h sum_c |q_hc k_jc|."""
+    qa, ka = np.abs(bf16_to_f64(q)), np.abs(bf16_to_f64(k))
+    return 2.0 ** -20 * ((ka @ qa.T) * np.asarray(w)[None, :]).sum(1) + 1e-30
+
+
+def attn_close(out, ref):
+    """Attention parity: max-abs error <= 2e-3 x RMS of the oracle output."""
+    rms = np.sqrt(np.mean(np.asarray(ref) ** 2))
+    assert np.max(np.abs(np.asarray(out) - ref)) <= 2e-3 * rms

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import synth
-from helpers import check_topk, dev, dev_bf16, host_bf16_bits
+from helpers import attn_close, check_topk, dev, dev_bf16, host_bf16_bits
 from oracle.csa2 import (LayerInputs, compress, decode_step, index_scores, indexer_k, quant_fp4)
 
 pytestmark = pytest.mark.gpu
@@ -36,11 +36,6 @@ def layer_inputs(wl, B, layers):
                                      q_idx=None if qi is None else dev_bf16(qi),
                                      w=None if w is None else dev(w)))
     return host, devl
-
-
-def attn_close(out, ref):
-    rms = np.sqrt(np.mean(ref ** 2))
-    assert np.max(np.abs(out - ref)) <= 2e-3 * rms
 
 
 def test_full_decode_4k_from_hidden_states():

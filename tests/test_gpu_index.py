@@ -3,8 +3,8 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import check_topk, dev, dev_bf16
-from oracle.codecs import bf16_to_f64, f64_to_bf16
+from helpers import check_topk, dev, dev_bf16, score_tol
+from oracle.codecs import f64_to_bf16
 from oracle.csa2 import build_pool, index_scores, reindex, visible_count
 
 pytestmark = pytest.mark.gpu
@@ -17,12 +17,6 @@ def bd():
 
 def rand_bf16(rng, shape, scale=1.0):
     return f64_to_bf16(rng.standard_normal(shape) * scale)
-
-
-def score_tol(q, w, k):
-    """fp32-accumulation bound: 2^-20 x sum_h w_h sum_c |q_hc k_jc|."""
-    qa, ka = np.abs(bf16_to_f64(q)), np.abs(bf16_to_f64(k))
-    return 2.0 ** -20 * ((ka @ qa.T) * np.asarray(w)[None, :]).sum(1) + 1e-30
 
 
 @pytest.mark.parametrize("B,N,h_i,d_i", [(2, 1000, 8, 128), (3, 300, 4, 64), (1, 5000, 16, 128),
