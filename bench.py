@@ -156,6 +156,111 @@ def cpu_baseline(wl, seconds):
                       f"({'+'.join(wl.layers)}, {wl.N} entries), {el:.1f}s, float64 numpy"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(wl) -> dict:
+    """Dense-contraction flops of one prefill chunk: the causal indexer scoring
+    (2 * h_i * d_i per visible (query, entry) pair) and the attention (2 * 2 * d
+    per (query, head, key) for Q·K and P·V, over K selected entries + its window)."""
+    vis = sum(min(wl.N, (t + 1) // wl.m) for t in range(wl.pos0, wl.T))
+    idx = 2 * wl.h_i * wl.d_i * vis
+    keys = sum(min(wl.K, min(wl.N, (t + 1) // wl.m)) + min(wl.n_win, t + 1) for t in range(wl.pos0, wl.T))
+    attn = len(wl.layers) * wl.H_q * 4 * wl.d * keys
+    comp = 2 * wl.chunk * wl.d_model * 2 * wl.d
+    return {"indexer": idx, "attention": attn, "compressor": comp, "visible_pairs": vis}
+
+
+def prefill_main(args, wl, torch, bd, sch):
+    """One prefill chunk (compress, FP4 + indexer keys, Full + Reuse layers), from a
+    captured graph; inputs resident in HBM.  value = chunk tokens / s."""
+    import synth
+    dev = torch.device("cuda")
+    N, n_pre, Tq, d = wl.N, wl.n_pre, wl.chunk, wl.d
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    Wik = bf(synth.w_ik(wl))
+    codes = torch.empty(1, N, d // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(1, N, d // 16, dtype=torch.uint8, device=dev)
+    kidx = torch.empty(1, N, wl.d_i, dtype=torch.bfloat16, device=dev)
+    bd.csa2_quant_fp4(tt(synth.main_kv(wl, 0, 0, n_pre)), codes=codes[0, :n_pre],
+                      scales=scales[0, :n_pre], W_ik=Wik, k_idx=kidx[0, :n_pre])
+    H = bf(synth.hidden(wl))
+    Wkv, Wz = (bf(x) for x in synth.compressor_weights(wl))
+    layers = []
+    for li, mode in enumerate(wl.layers):
+        layers.append(sch.LayerBuffers(
+            bf(synth.q_main(wl, li, 0, Tq)[None]), tt(synth.swa_tokens(wl, li, 0)[None]),
+            bf(synth.q_index(wl, li, 0, Tq)[None]) if mode == "F" else None,
+            tt(synth.head_weights(wl, li, 0, Tq)[None]) if mode == "F" else None))
+    torch.cuda.synchronize()
+    log(f"prefill inputs built: {Tq} queries, {len(layers)} layers")
+    run = sch.PrefillChunk(wl.layers, N, n_pre, Tq, d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K, wl.m,
+                           wl.pos0, wl.swa_pos0, wl.n_win, wl.rope_dim)
+    step = lambda: run.step(H, Wkv, Wz, Wik, codes, scales, kidx, layers)
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        step = g.replay
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    step_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    log(f"timed {args.steps} chunks: {step_s * 1e6:.1f} us/chunk")
+    # the indexer-scoring launch alone (the contraction the MFMA roofline is quoted for)
+    lb = layers[0]
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        bd.csa2_index_full(lb.q_idx, lb.w, kidx, q_pos=run.q_pos, m=wl.m, scores=run.scores)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(args.kernel_reps):
+        bd.csa2_index_full(lb.q_idx, lb.w, kidx, q_pos=run.q_pos, m=wl.m, scores=run.scores)
+    e1.record(st)
+    e1.synchronize()
+    idx_s = e0.elapsed_time(e1) / args.kernel_reps / 1e3
+    fl = prefill_flops(wl)
+    achieved = fl["indexer"] / idx_s / 1e12
+    log(f"indexer: {idx_s * 1e6:.1f} us/launch, {achieved:.1f} TFLOP/s")
+    out = {
+        "metric": "CSA2 prefill chunk tokens/s; indexer MFMA TFLOP/s vs MI355X bf16 peak",
+        "value": Tq / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "chunk_tokens": Tq, "context_tokens": wl.T,
+                   "entries": N, "m": wl.m, "d": d, "d_model": wl.d_model,
+                   "indexer": f"{wl.h_i}x{wl.d_i}", "heads": wl.H_q, "top_k": wl.K,
+                   "schedule": wl.schedule, "graph": not args.no_graph,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "indexer scoring (causal Q·K^T, bf16)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "launch_us": idx_s * 1e6, "algorithmic_flops_per_launch": fl["indexer"]},
+        "chunk_flops": fl,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -173,6 +278,8 @@ def main():
         sys.exit(1)
     bd.lib()
     wl = synth.workload(args.workload)
+    if wl.chunk:
+        return prefill_main(args, wl, torch, bd, sch)
     if wl.T:
         raise SystemExit("workloads built from hidden states are parity cases, not bench lines")
     log(f"workload {wl.name}: B={wl.B} N={wl.N} d={wl.d} schedule={wl.schedule}")

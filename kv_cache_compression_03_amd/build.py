@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
 
-SOURCES = ["api.cpp", "quant.hip", "compress.hip", "index.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.cpp", "quant.hip", "compress.hip", "index.hip", "index_prefill.hip", "topk.hip",
+           "attn.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

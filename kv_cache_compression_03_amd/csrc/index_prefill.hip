@@ -1,0 +1,204 @@
+// Indexer scores of many queries at once (prefill): a causal bf16 contraction on
+// MFMA.  s_{t,j} = sum_h w_{t,h} * max(0, q_{t,h} · k_j) for every entry j visible
+// to query t (p_j <= t), -inf for the others.
+//
+// [deep-dive §3.1, §3.3] the indexer scores every visible entry of every query;
+// with thousands of queries the scores form a dense [Tq*h_i, d_i] x [d_i, N]
+// product (rows = (query, head) pairs), so this is MFMA work.
+//
+// A workgroup owns 256 rows (256 / h_i queries) and a range of keys.  Each of
+// its four waves keeps its 64 rows of Q in registers (the A operands) for the
+// whole range; the keys pass through LDS in tiles of 64, double-buffered, each
+// staged once and read by all four waves as B operands.  Per tile a wave runs
+// 4 row tiles x 4 key tiles x d_i/32 MFMA 16x16x32 steps; the epilogue applies
+// ReLU, the head weights and the head sum on the MFMA output (a lane holds 4
+// heads of one query for one key; the other heads of that query sit in the
+// lanes 16 and 32 apart) and stores the scores with the causal mask applied.
+// Key tiles that no query of the workgroup can see are filled with -inf
+// without any MFMA.
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfRows = 256;  // (query, head) rows per workgroup, 64 per wave
+constexpr int kPfKeys = 64;   // keys per staged tile
+#ifndef CSA2_PF_SPLIT
+#define CSA2_PF_SPLIT 4096    // keys per workgroup
+#endif
+
+template <int HI, int DI>
+__global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, const int* __restrict__ q_pos, int m, int Tq, int N,
+    float* __restrict__ scores) {
+  constexpr int QPW = kPfRows / HI;         // queries per workgroup
+  constexpr int GPQ = HI / 4;               // lane groups holding one query's heads
+  constexpr int KS = DI / 32;               // MFMA reduction steps
+  constexpr int RT = 4;                     // 16-row tiles per wave
+  constexpr int CT = kPfKeys / 16;          // 16-key tiles per staged tile
+  constexpr int KP = DI + 8;                // staged key pitch (bf16): 16 B pad, conflict-free reads
+  constexpr int CPK = DI / 8;               // 16-byte chunks per key
+  constexpr int CPT = kPfKeys * CPK / (kPfWaves * 64);  // chunks each thread stages
+  static_assert(GPQ >= 1 && GPQ <= 4, "h_i must be 4, 8 or 16");
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kPfKeys * KP];
+  __shared__ int s_vmax[kPfWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
+  const int b = blockIdx.z;
+  const int qb0 = blockIdx.y * QPW;
+  const int key_lo = blockIdx.x * CSA2_PF_SPLIT;
+  const int key_hi = min(N, key_lo + CSA2_PF_SPLIT);
+
+  // ---- A operands: row 64*wave + 16*rt + col is (query row/HI, head row%HI); the
+  // reduction slots of step s, lane group g are dims 32s + 8g .. 32s + 8g + 7
+  bf16x8_t qa[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 64 * wave + 16 * rt + col;
+    const int t = qb0 + row / HI;
+    const uint4* qr =
+        reinterpret_cast<const uint4*>(q_idx + (((size_t)b * Tq + min(t, Tq - 1)) * HI + row % HI) * DI);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[rt][s] = as_bf16x8(t < Tq ? qr[4 * s + g] : make_uint4(0, 0, 0, 0));
+  }
+  // ---- output side: lane holds rows 64*wave + 16*rt + 4g + i (i = 0..3)
+  float wv[RT][4];
+  int nv[RT];
+  bool lv[RT];
+  float* srow[RT];
+  int vmax = 0;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r0 = 64 * wave + 16 * rt + 4 * g;
+    const int t = qb0 + r0 / HI;
+    const bool live = t < Tq;
+    const size_t qrow = (size_t)b * Tq + (live ? t : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[rt][i] = live ? w[qrow * HI + (r0 + i) % HI] : 0.0f;
+    int n = 0;
+    if (live) {
+      if (q_pos != nullptr) {
+        const long long v = ((long long)q_pos[qrow] + 1) / m;  // entries with p_j <= t
+        n = (int)(v < 0 ? 0 : (v > N ? N : v));
+      } else {
+        n = N;
+      }
+    }
+    nv[rt] = n;
+    lv[rt] = live;
+    vmax = max(vmax, n);
+    srow[rt] = scores + qrow * N;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o));
+  if (lane == 0) s_vmax[wave] = vmax;
+  const bool writer = (g % GPQ) == 0;
+
+  // staging of key tile `tile`: thread tid moves 16-byte chunks tid + u*256
+  // (key c / CPK, dims (c % CPK)*8 ..) through registers into LDS
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 stg[CPT];
+#define CSA2_PF_FETCH(tile_)                                                                   \
+  _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                            \
+    const int c = tid + u * (kPfWaves * 64);                                                   \
+    const int j = min(key_lo + (tile_) * kPfKeys + c / CPK, N - 1);                            \
+    stg[u] = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)b * N + j) * DI + (c % CPK) * 8); \
+  }
+#define CSA2_PF_STASH(buf_)                                                                    \
+  _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                            \
+    const int c = tid + u * (kPfWaves * 64);                                                   \
+    *reinterpret_cast<u32x4*>(&kt[(buf_)][(c / CPK) * KP + (c % CPK) * 8]) = stg[u];           \
+  }
+
+  __syncthreads();  // s_vmax
+  const int vis = min(key_hi, max(max(s_vmax[0], s_vmax[1]), max(s_vmax[2], s_vmax[3])));
+  const int n_comp = vis > key_lo ? (vis - key_lo + kPfKeys - 1) / kPfKeys : 0;
+
+  if (n_comp > 0) {
+    CSA2_PF_FETCH(0)
+    CSA2_PF_STASH(0)
+  }
+  lds_barrier();
+  for (int tile = 0; tile < n_comp; ++tile) {
+    const int buf = tile & 1;
+    // the next tile's keys are in flight during this tile's MFMAs; fetched and
+    // stashed on every pass (the last one re-stages its own tile into the idle
+    // buffer) so that no wait in the loop has to assume loads left pending
+    CSA2_PF_FETCH(min(tile + 1, n_comp - 1))
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    f32x4_t acc[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8_t kb =
+            *reinterpret_cast<const bf16x8_t*>(&kt[buf][(16 * ct + col) * KP + 32 * s + 8 * g]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][ct] = mfma16x16x32(qa[rt][s], kb, acc[rt][ct]);
+      }
+    }
+    // ---- epilogue: ReLU, head weights, head sum, causal mask
+    const int key0 = key_lo + tile * kPfKeys;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float p = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p = fmaf(wv[rt][i], fmaxf(acc[rt][ct][i], 0.0f), p);
+        if (GPQ >= 2) p += __shfl_xor(p, 16);
+        if (GPQ >= 4) p += __shfl_xor(p, 32);
+        const int j = key0 + 16 * ct + col;
+        if (writer && lv[rt] && j < N) srow[rt][j] = j < nv[rt] ? p : -INFINITY;
+      }
+    }
+    CSA2_PF_STASH(buf ^ 1)
+    lds_barrier();
+  }
+#undef CSA2_PF_FETCH
+#undef CSA2_PF_STASH
+  // ---- key tiles no query of this workgroup can see
+  const int tail = key_lo + n_comp * kPfKeys;
+  if (tail < key_hi) {
+    for (int qq = 0; qq < QPW; ++qq) {
+      const int t = qb0 + qq;
+      if (t >= Tq) break;
+      float* r = scores + ((size_t)b * Tq + t) * N;
+      for (int j = tail + tid; j < key_hi; j += kPfWaves * 64) r[j] = -INFINITY;
+    }
+  }
+}
+
+bool index_prefill_supported(int Tq, int h_i, int d_i, const int* gather) {
+  return gather == nullptr && (long long)Tq * h_i >= kPfRows && (h_i == 4 || h_i == 8 || h_i == 16) &&
+         (d_i == 64 || d_i == 128);
+}
+
+hipError_t launch_index_prefill(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                                const int* q_pos, int m, int B, int Tq, int N, int h_i, int d_i,
+                                float* scores, hipStream_t st) {
+  if (B == 0 || Tq == 0 || N == 0) return hipSuccess;
+  const int qpw = kPfRows / h_i;
+  dim3 grid((unsigned)((N + CSA2_PF_SPLIT - 1) / CSA2_PF_SPLIT), (unsigned)((Tq + qpw - 1) / qpw),
+            (unsigned)B),
+      block(kPfWaves * 64);
+#define CSA2_PF(HI_, DI_)                                                                      \
+  hipLaunchKernelGGL((index_prefill_kernel<HI_, DI_>), grid, block, 0, st, q_idx, w, k_idx, q_pos, \
+                     m, Tq, N, scores)
+  if (h_i == 8 && d_i == 128) CSA2_PF(8, 128);
+  else if (h_i == 8 && d_i == 64) CSA2_PF(8, 64);
+  else if (h_i == 4 && d_i == 128) CSA2_PF(4, 128);
+  else if (h_i == 4 && d_i == 64) CSA2_PF(4, 64);
+  else if (h_i == 16 && d_i == 128) CSA2_PF(16, 128);
+  else CSA2_PF(16, 64);
+#undef CSA2_PF
+  return hipGetLastError();
+}
+
+}  // namespace csa2

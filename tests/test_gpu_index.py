@@ -58,6 +58,38 @@ def test_scores_with_positions():
             check_topk(sel[b, t], ref, 512, n_vis=n)
 
 
+@pytest.mark.parametrize("B,Tq,N,h_i,d_i,m,pos", [
+    (1, 100, 5000, 8, 128, 2, "rand"), (2, 70, 4100, 4, 64, 1, "rand"),
+    (1, 40, 9000, 16, 128, 2, "causal"), (1, 64, 300, 8, 64, 1, "none"),
+    (2, 33, 8193, 8, 128, 1, "causal"), (1, 17, 4096, 16, 64, 2, "rand")])
+def test_prefill_scores(B, Tq, N, h_i, d_i, m, pos):
+    """Many queries at once (the MFMA contraction path): every score of every row,
+    visible ones within the fp32 bound and the rest -inf; Top-K over the visible range."""
+    rng = np.random.default_rng(Tq * N + h_i)
+    q = rand_bf16(rng, (B, Tq, h_i, d_i))
+    w = rng.random((B, Tq, h_i)).astype(np.float32)
+    k = rand_bf16(rng, (B, N, d_i))
+    if pos == "none":
+        qp = None
+    elif pos == "causal":  # a chunk whose last query sees every entry
+        qp = np.broadcast_to(np.arange(m * N - Tq, m * N, dtype=np.int32), (B, Tq)).copy()
+    else:  # positions in no particular order, some seeing nothing
+        qp = rng.integers(-3, m * N + 40, (B, Tq)).astype(np.int32)
+    sc = bd().csa2_index_full(dev_bf16(q), dev(w), dev_bf16(k), q_pos=None if qp is None else dev(qp), m=m)
+    nv = np.array([[N if qp is None else visible_count(int(qp[b, t]), N, m) for t in range(Tq)]
+                   for b in range(B)], np.int32)
+    sel = bd().csa2_topk(sc.view(B * Tq, N), 64, valid_len=dev(nv.reshape(-1)))
+    torch.cuda.synchronize()
+    sc, sel = sc.cpu().numpy(), sel.cpu().numpy().reshape(B, Tq, 64)
+    for b in range(B):
+        for t in range(Tq):
+            n = nv[b, t]
+            ref = index_scores(q[b, t], w[b, t], k[b])
+            assert np.all(np.isneginf(sc[b, t, n:]))
+            assert np.all(np.abs(sc[b, t, :n] - ref[:n]) <= score_tol(q[b, t], w[b, t], k[b])[:n])
+            check_topk(sel[b, t], ref, 64, n_vis=n)
+
+
 @pytest.mark.parametrize("R,N,K,kind", [(3, 5000, 512, "gauss"), (2, 65536, 512, "gauss"),
                                         (1, 1 << 20, 512, "gauss"), (2, 65536, 512, "ties"),
                                         (4, 8192, 2048, "ties"), (2, 20000, 1, "gauss"),
