@@ -120,7 +120,7 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
                                int B, int Tq, int N, int L, int h_i, int d_i, float* scores,
                                hipStream_t st) {
   if (B == 0 || Tq == 0 || L == 0) return hipSuccess;
-  if (L == N && index_prefill_supported(Tq, h_i, d_i, gather))
+  if (L == N && index_prefill_supported(Tq, N, h_i, d_i, gather))
     return launch_index_prefill(q_idx, w, k_idx, q_pos, m, B, Tq, N, h_i, d_i, scores, st);
   const int qpt = 16 / h_i;
   const int qgroups = (Tq + qpt - 1) / qpt;

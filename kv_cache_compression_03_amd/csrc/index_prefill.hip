@@ -10,10 +10,12 @@
 // its four waves keeps its 64 rows of Q in registers (the A operands) for the
 // whole range; the keys pass through LDS in tiles of 64, double-buffered, each
 // staged once and read by all four waves as B operands.  Per tile a wave runs
-// 4 row tiles x 4 key tiles x d_i/32 MFMA 16x16x32 steps; the epilogue applies
-// ReLU, the head weights and the head sum on the MFMA output (a lane holds 4
-// heads of one query for one key; the other heads of that query sit in the
-// lanes 16 and 32 apart) and stores the scores with the causal mask applied.
+// 4 row tiles x 4 key tiles x d_i/32 MFMA 16x16x32 steps.  Rows are assigned
+// so that a group of h_i/4 row tiles holds 4 queries: row 4q + i of the group's
+// tile u is head 4u + i of query q.  An MFMA output lane (lane group g, key
+// column c) then holds, across the group's tiles, every head of query g for
+// key c, and applies ReLU, the head weights, the head sum and the causal mask
+// on its own before storing the score.
 // Key tiles that no query of the workgroup can see are filled with -inf
 // without any MFMA.
 #include "common.h"
@@ -24,9 +26,16 @@ namespace csa2 {
 constexpr int kPfWaves = 4;
 constexpr int kPfRows = 256;  // (query, head) rows per workgroup, 64 per wave
 constexpr int kPfKeys = 64;   // keys per staged tile
+constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family: 32-bit data)
+constexpr int kOutOfRange = 0x7FFFFFF0;      // a byte offset past any score buffer of this kernel
 #ifndef CSA2_PF_SPLIT
 #define CSA2_PF_SPLIT 4096    // keys per workgroup
 #endif
+
+// max(x, 0) in one integer instruction: a float with the sign bit set is a
+// negative int32 (that includes -0), any other float keeps its bits.  (fmaxf
+// would first quiet a NaN input, one more instruction per element.)
+CSA2_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 template <int HI, int DI>
 __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
@@ -34,14 +43,15 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
     const uint16_t* __restrict__ k_idx, const int* __restrict__ q_pos, int m, int Tq, int N,
     float* __restrict__ scores) {
   constexpr int QPW = kPfRows / HI;         // queries per workgroup
-  constexpr int GPQ = HI / 4;               // lane groups holding one query's heads
+  constexpr int TPG = HI / 4;               // row tiles per group of 4 queries
   constexpr int KS = DI / 32;               // MFMA reduction steps
   constexpr int RT = 4;                     // 16-row tiles per wave
   constexpr int CT = kPfKeys / 16;          // 16-key tiles per staged tile
   constexpr int KP = DI + 8;                // staged key pitch (bf16): 16 B pad, conflict-free reads
   constexpr int CPK = DI / 8;               // 16-byte chunks per key
   constexpr int CPT = kPfKeys * CPK / (kPfWaves * 64);  // chunks each thread stages
-  static_assert(GPQ >= 1 && GPQ <= 4, "h_i must be 4, 8 or 16");
+  constexpr int NG = RT / TPG;              // query groups per wave
+  static_assert(TPG >= 1 && TPG <= 4 && RT % TPG == 0, "h_i must be 4, 8 or 16");
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][kPfKeys * KP];
   __shared__ int s_vmax[kPfWaves];
 
@@ -51,50 +61,74 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
   const int key_lo = blockIdx.x * CSA2_PF_SPLIT;
   const int key_hi = min(N, key_lo + CSA2_PF_SPLIT);
 
-  // ---- A operands: row 64*wave + 16*rt + col is (query row/HI, head row%HI); the
-  // reduction slots of step s, lane group g are dims 32s + 8g .. 32s + 8g + 7
+  // ---- A operands: row r of row tile rt (rt = group * TPG + u) is head 4u + r%4 of
+  // query 64*wave/HI + 4*group + r/4; the reduction slots of step s, lane group
+  // g are dims 32s + 8g .. 32s + 8g + 7
+  const int wq0 = qb0 + (64 * wave) / HI;  // first query of this wave
   bf16x8_t qa[RT][KS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int row = 64 * wave + 16 * rt + col;
-    const int t = qb0 + row / HI;
+    const int t = wq0 + 4 * (rt / TPG) + col / 4;
+    const int h = 4 * (rt % TPG) + col % 4;
     const uint4* qr =
-        reinterpret_cast<const uint4*>(q_idx + (((size_t)b * Tq + min(t, Tq - 1)) * HI + row % HI) * DI);
+        reinterpret_cast<const uint4*>(q_idx + (((size_t)b * Tq + min(t, Tq - 1)) * HI + h) * DI);
 #pragma unroll
     for (int s = 0; s < KS; ++s) qa[rt][s] = as_bf16x8(t < Tq ? qr[4 * s + g] : make_uint4(0, 0, 0, 0));
   }
-  // ---- output side: lane holds rows 64*wave + 16*rt + 4g + i (i = 0..3)
-  float wv[RT][4];
-  int nv[RT];
-  bool lv[RT];
-  float* srow[RT];
+  // Wait for Q here, once: otherwise the wait for it lands inside the key loop,
+  // where it would also wait for that loop's score stores.
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qa[rt][s]));
+  // ---- output side: in group n, lane group g holds query wq0 + 4n + g; element i of
+  // its tile u is head 4u + i
+  float wv[NG][TPG][4];
+  int nv[NG];
   int vmax = 0;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r0 = 64 * wave + 16 * rt + 4 * g;
-    const int t = qb0 + r0 / HI;
+  for (int n = 0; n < NG; ++n) {
+    const int t = wq0 + 4 * n + g;
     const bool live = t < Tq;
     const size_t qrow = (size_t)b * Tq + (live ? t : 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[rt][i] = live ? w[qrow * HI + (r0 + i) % HI] : 0.0f;
-    int n = 0;
+    for (int u = 0; u < TPG; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[n][u][i] = live ? w[qrow * HI + 4 * u + i] : 0.0f;
+    int c = 0;
     if (live) {
       if (q_pos != nullptr) {
         const long long v = ((long long)q_pos[qrow] + 1) / m;  // entries with p_j <= t
-        n = (int)(v < 0 ? 0 : (v > N ? N : v));
+        c = (int)(v < 0 ? 0 : (v > N ? N : v));
       } else {
-        n = N;
+        c = N;
       }
     }
-    nv[rt] = n;
-    lv[rt] = live;
-    vmax = max(vmax, n);
-    srow[rt] = scores + qrow * N;
+    nv[n] = c;
+    vmax = max(vmax, c);
+  }
+  // the same for the head weights and visible counts (loaded before the loop)
+#pragma unroll
+  for (int n = 0; n < NG; ++n) {
+#pragma unroll
+    for (int u = 0; u < TPG; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(wv[n][u][i]));
+    asm volatile("" : "+v"(nv[n]));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o));
   if (lane == 0) s_vmax[wave] = vmax;
-  const bool writer = (g % GPQ) == 0;
+  // The workgroup's score rows as one raw buffer: a store whose offset falls
+  // outside it is dropped by the hardware range check, so masked lanes (keys
+  // past N, rows past Tq) are given an out-of-range offset and no store sits
+  // behind a branch.
+  const int rows_here = min(QPW, Tq - qb0);
+  const __amdgpu_buffer_rsrc_t srsc = __builtin_amdgcn_make_buffer_rsrc(
+      scores + ((size_t)b * Tq + qb0) * N, (short)0, rows_here * N * (int)sizeof(float), kRawBufferWord3);
+  int roff[NG];  // byte offset of this lane's query row in the buffer, per group
+#pragma unroll
+  for (int n = 0; n < NG; ++n) roff[n] = (wq0 - qb0 + 4 * n + g) * N * (int)sizeof(float);
 
   // staging of key tile `tile`: thread tid moves 16-byte chunks tid + u*256
   // (key c / CPK, dims (c % CPK)*8 ..) through registers into LDS
@@ -143,19 +177,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
         for (int rt = 0; rt < RT; ++rt) acc[rt][ct] = mfma16x16x32(qa[rt][s], kb, acc[rt][ct]);
       }
     }
-    // ---- epilogue: ReLU, head weights, head sum, causal mask
+    // ---- epilogue: ReLU, head weights, head sum, causal mask (all within the lane)
     const int key0 = key_lo + tile * kPfKeys;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int n = 0; n < NG; ++n) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         float p = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p = fmaf(wv[rt][i], fmaxf(acc[rt][ct][i], 0.0f), p);
-        if (GPQ >= 2) p += __shfl_xor(p, 16);
-        if (GPQ >= 4) p += __shfl_xor(p, 32);
+        for (int u = 0; u < TPG; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p = fmaf(wv[n][u][i], relu(acc[n * TPG + u][ct][i]), p);
         const int j = key0 + 16 * ct + col;
-        if (writer && lv[rt] && j < N) srow[rt][j] = j < nv[rt] ? p : -INFINITY;
+        const int off = j < N ? roff[n] + j * (int)sizeof(float) : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(j < nv[n] ? p : -INFINITY), srsc, off, 0, 0);
       }
     }
     CSA2_PF_STASH(buf ^ 1)
@@ -175,9 +210,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
   }
 }
 
-bool index_prefill_supported(int Tq, int h_i, int d_i, const int* gather) {
+bool index_prefill_supported(int Tq, int N, int h_i, int d_i, const int* gather) {
+  // a workgroup's score rows (at most 64 of N floats) must fit one raw buffer below kOutOfRange
   return gather == nullptr && (long long)Tq * h_i >= kPfRows && (h_i == 4 || h_i == 8 || h_i == 16) &&
-         (d_i == 64 || d_i == 128);
+         (d_i == 64 || d_i == 128) && (long long)(kPfRows / 4) * N * sizeof(float) < kOutOfRange;
 }
 
 hipError_t launch_index_prefill(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,

@@ -24,7 +24,7 @@ hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_mode
 // index.hip: scores[b, t, i] for rows i < L of sequence b (rows gathered through
 // `gather` when not null).
 // Prefill indexer (index_prefill.hip): many queries, no gather.
-bool index_prefill_supported(int Tq, int h_i, int d_i, const int* gather);
+bool index_prefill_supported(int Tq, int N, int h_i, int d_i, const int* gather);
 hipError_t launch_index_prefill(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                                 const int* q_pos, int m, int B, int Tq, int N, int h_i, int d_i,
                                 float* scores, hipStream_t st);
