@@ -150,18 +150,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
   const int vis = min(key_hi, max(max(s_vmax[0], s_vmax[1]), max(s_vmax[2], s_vmax[3])));
   const int n_comp = vis > key_lo ? (vis - key_lo + kPfKeys - 1) / kPfKeys : 0;
 
+  // Pipeline: tile t is multiplied from LDS buffer t&1; at the end of the pass tile
+  // t+1 (whose loads were issued at the end of the previous pass) is stashed into
+  // the other buffer and tile t+2's loads are issued, to fly during the next pass.
+  // Stash and fetch run on every pass, clamped to the last tile, and every path
+  // into the stash has the same loads and score stores before it, so its wait
+  // covers the loads only.
   if (n_comp > 0) {
     CSA2_PF_FETCH(0)
     CSA2_PF_STASH(0)
+    CSA2_PF_FETCH(min(1, n_comp - 1))
   }
   lds_barrier();
   for (int tile = 0; tile < n_comp; ++tile) {
     const int buf = tile & 1;
-    // the next tile's keys are in flight during this tile's MFMAs; fetched and
-    // stashed on every pass (the last one re-stages its own tile into the idle
-    // buffer) so that no wait in the loop has to assume loads left pending
-    CSA2_PF_FETCH(min(tile + 1, n_comp - 1))
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
     f32x4_t acc[RT][CT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -193,7 +195,10 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(j < nv[n] ? p : -INFINITY), srsc, off, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // stash after the stores
+    // buffer buf^1 was last read in pass tile-1, before that pass's barrier
     CSA2_PF_STASH(buf ^ 1)
+    CSA2_PF_FETCH(min(tile + 2, n_comp - 1))
     lds_barrier();
   }
 #undef CSA2_PF_FETCH
