@@ -12,8 +12,10 @@
 // the score ties break to the lower index.
 //
 // Rows with at most kTopkCap visible entries are selected whole in LDS (one
-// 1024-thread workgroup per row: radix select of the K-th key, then ranks).  Longer rows (decode over 64K-1M
-// entries, a handful of rows) first go through two wide passes:
+// 1024-thread workgroup per row: radix select of the K-th key, then ranks).  Rows
+// of up to kRowCap entries are thinned to candidates inside that same workgroup
+// (below).  Longer rows (decode over 64K-1M entries, a handful of rows) first go
+// through two wide passes:
 //   chunkmax: split the row into C >= K chunks and take each chunk's maximum;
 //   filter:   T = min of the chunk maxima.  Those C maxima are C distinct entries
 //             scoring >= T, so the K-th best score is >= T and every entry below
@@ -30,8 +32,12 @@ constexpr int kSelThreads = 1024;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Calls whose rows hold at most kRowCap entries run the one-pass row kernel
+// (no workspace); longer rows take the two wide passes first.
+constexpr int kRowCap = 16384;
+
 size_t topk_ws_bytes(int R, int N, int K) {
-  if (N <= kTopkCap) return 0;
+  if (N <= kRowCap) return 0;
   size_t b = 0;
   b += align256((size_t)R * 2 * K * sizeof(float));
   b += align256((size_t)R * sizeof(int));
@@ -221,15 +227,43 @@ CSA2_DEV void radix_select_row(const float* __restrict__ row, int n, int k, int*
   }
 }
 
-// The k-th largest of `total` unique 64-bit keys in LDS, by 8-bit digits from the top;
-// stops early once a digit's bucket is taken whole.  Returns T such that exactly k keys
-// are >= T.
+// The k-th largest of `total` unique 64-bit keys in LDS, by 8-bit digits; the bits
+// every key shares (scores of one magnitude share their top bits) are skipped, so
+// the first digit already spreads the keys.  Stops early once a digit's bucket is
+// taken whole.  Returns T such that exactly k keys are >= T.
 CSA2_DEV unsigned long long radix_kth_u64(const unsigned long long* keys, int total, int k,
                                           uint32_t* hist, unsigned long long* bcast) {
   const int tid = threadIdx.x, lane = tid & 63;
-  unsigned long long prefix = 0ull, mask = 0ull;
+  if (tid == 0) {
+    bcast[2] = 0ull;
+    bcast[3] = ~0ull;
+  }
+  __syncthreads();
+  // common high bits: OR and AND of all keys agree exactly where every key agrees
+  unsigned long long kor = 0ull, kand = ~0ull;
+  for (int i = tid; i < total; i += kSelThreads) {
+    kor |= keys[i];
+    kand &= keys[i];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kor |= __shfl_xor(kor, o);
+    kand &= __shfl_xor(kand, o);
+  }
+  if (lane == 0) {
+    atomicOr(reinterpret_cast<unsigned long long*>(&bcast[2]), kor);
+    atomicAnd(reinterpret_cast<unsigned long long*>(&bcast[3]), kand);
+  }
+  __syncthreads();
+  const unsigned long long diff = bcast[2] ^ bcast[3];
+  const int top = diff ? 63 - __clzll(diff) : 0;  // highest bit where keys differ
+  unsigned long long mask = diff ? ~0ull << (top + 1) : ~0ull;
+  if (top == 63) mask = 0ull;
+  unsigned long long prefix = bcast[3] & mask;
   int need = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  __syncthreads();
+  for (int shift = top - 7; shift > -8; shift -= 8) {
+    if (shift < 0) shift = 0;
     if (tid < 256) hist[tid] = 0u;
     __syncthreads();
     for (int i = tid; i < total; i += kSelThreads) {
@@ -264,12 +298,42 @@ CSA2_DEV unsigned long long radix_kth_u64(const unsigned long long* keys, int to
     const unsigned long long dsel = bcast[0];
     const int need2 = (int)bcast[1], bucket = (int)bcast[2];
     __syncthreads();
-    prefix |= dsel << shift;
+    prefix = (prefix & ~(255ull << shift)) | (dsel << shift);
     mask |= 255ull << shift;
     need = need2;
-    if (bucket == need) break;  // the whole bucket is taken: keys >= prefix are exactly k
+    if (bucket == need || shift == 0) break;  // the whole bucket is taken: keys >= prefix are exactly k
   }
   return prefix;
+}
+
+// Writes the k chosen indices of a row in ascending order (rank = number of
+// chosen indices below), -1 in slots k..K-1.  chosen[k .. 4*ceil(k/4)) must hold
+// INT_MAX; the count reads four chosen indices per LDS access.
+CSA2_DEV void write_ranked(const int* chosen, int k, int K, int* orow, const int* cmap_row) {
+  const int4* c4 = reinterpret_cast<const int4*>(chosen);
+  const int k4 = (k + 3) / 4;
+  for (int i = threadIdx.x; i < K; i += kSelThreads) {
+    if (i < k) {
+      const int v = chosen[i];
+      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+#pragma unroll 4
+      for (int j = 0; j < k4; ++j) {
+        const int4 c = c4[j];
+        r0 += c.x < v;
+        r1 += c.y < v;
+        r2 += c.z < v;
+        r3 += c.w < v;
+      }
+      orow[r0 + r1 + r2 + r3] = cmap_row ? cmap_row[v] : v;
+    } else {
+      orow[i] = -1;
+    }
+  }
+}
+
+CSA2_DEV void pad_chosen(int* chosen, int k) {
+  const int k4 = 4 * ((k + 3) / 4);
+  if ((int)threadIdx.x < k4 - k) chosen[k + threadIdx.x] = 0x7FFFFFFF;
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
@@ -277,7 +341,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const int* __restrict__ cand_map, int K, int* __restrict__ out, const int* __restrict__ cnt,
     const float* __restrict__ cscore, const int* __restrict__ cidx) {
   extern __shared__ unsigned long long keys[];  // kTopkCap keys (64 KB)
-  __shared__ int chosen[2048];
+  __shared__ __attribute__((aligned(16))) int chosen[2048];
   __shared__ uint32_t hist[256];
   __shared__ unsigned long long bcast[4];
   __shared__ int misc[32];
@@ -307,24 +371,129 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     }
     __syncthreads();
   }
-  // output in ascending index order: rank = number of chosen indices below
-  int* orow = out + (size_t)r * K;
-  for (int i = tid; i < K; i += kSelThreads) {
-    if (i < k) {
-      const int v = chosen[i];
-      int rank = 0;
-      for (int j = 0; j < k; ++j) rank += chosen[j] < v ? 1 : 0;
-      orow[rank] = cand_map ? cand_map[(size_t)r * N + v] : v;
-    } else {
-      orow[i] = -1;
+  // output in ascending index order
+  pad_chosen(chosen, k);
+  __syncthreads();
+  write_ranked(chosen, k, K, out + (size_t)r * K, cand_map ? cand_map + (size_t)r * N : nullptr);
+}
+
+// Rows of at most kRowCap entries (prefill: thousands of rows of 12K-16K visible
+// entries) in one pass, one workgroup per row: the row is staged in LDS, the
+// minimum T of C >= K chunk maxima bounds the K-th best score from below, the
+// entries scoring >= T become 64-bit keys in LDS, and the K-th key is found by
+// radix select as for short rows.  A row whose candidates overflow (heavy ties)
+// falls back to the exact whole-row select.
+
+__global__ __launch_bounds__(kSelThreads) void topk_row_kernel(
+    const float* __restrict__ scores, int N, const int* __restrict__ valid_len,
+    const int* __restrict__ cand_map, int K, int* __restrict__ out) {
+  __shared__ float s_row[kRowCap];                // 64 KB
+  __shared__ unsigned long long keys[kTopkCap];   // 64 KB
+  __shared__ __attribute__((aligned(16))) int chosen[2048];
+  __shared__ uint32_t hist[256];
+  __shared__ unsigned long long bcast[4];
+  __shared__ int misc[32];
+  __shared__ float red[kSelThreads / 64];
+  __shared__ uint32_t bitmap[kRowCap / 32];
+  __shared__ int wsum[kSelThreads / 64];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = row_len(valid_len, r, N);
+  const int k = min(K, n);
+  const float* row = scores + (size_t)r * N;
+  int total;
+  if (n <= kTopkCap) {
+    for (int i = tid; i < n; i += kSelThreads) keys[i] = make_key(row[i], i);
+    total = n;
+  } else {
+    for (int i = tid; i < n; i += kSelThreads) s_row[i] = row[i];
+    if (tid == 0) misc[0] = 0;
+    __syncthreads();
+    // C >= K chunks of clen entries: their maxima are C distinct entries, so the
+    // K-th best score is at least the smallest of them
+    const int clen = n / K;
+    const int C = (n + clen - 1) / clen;
+    float mn = INFINITY;
+    for (int c = tid; c < C; c += kSelThreads) {
+      const int lo = c * clen, hi = min(lo + clen, n);
+      float mx = -INFINITY;
+#pragma unroll 8
+      for (int i = lo; i < hi; ++i) mx = fmaxf(mx, s_row[i]);
+      mn = fminf(mn, mx);
     }
+    mn = wave_min(mn);
+    if (lane == 0) red[wave] = mn;
+    __syncthreads();
+    float T = red[0];
+#pragma unroll
+    for (int w2 = 1; w2 < kSelThreads / 64; ++w2) T = fminf(T, red[w2]);
+    const uint32_t tk = mono_key(T);
+    for (int base = 0; base < n; base += kSelThreads) {
+      const int i = base + tid;
+      const float sv = i < n ? s_row[i] : 0.0f;
+      const bool take = i < n && mono_key(sv) >= tk;
+      const unsigned long long m = __ballot(take);
+      int wpos = 0;
+      if (lane == 0 && m) wpos = atomicAdd(&misc[0], __popcll(m));
+      wpos = __shfl(wpos, 0);
+      const int pos = wpos + __popcll(m & ((1ull << lane) - 1ull));
+      if (take && pos < kTopkCap) keys[pos] = make_key(sv, i);
+    }
+    __syncthreads();
+    total = misc[0];
+    __syncthreads();
   }
+  if (total > kTopkCap || total < k) {
+    int* sel = reinterpret_cast<int*>(keys + 1024);
+    radix_select_row(row, n, k, sel, reinterpret_cast<uint32_t*>(keys), misc);
+    for (int i = tid; i < k; i += kSelThreads) chosen[i] = sel[i];
+    __syncthreads();
+  } else {
+    if (tid == 0) misc[0] = 0;
+    __syncthreads();
+    const unsigned long long T = k > 0 ? radix_kth_u64(keys, total, k, hist, bcast) : ~0ull;
+    for (int i = tid; i < total; i += kSelThreads) {
+      const unsigned long long key = keys[i];
+      if (key >= T) chosen[atomicAdd(&misc[0], 1)] = key_index(key);
+    }
+    __syncthreads();
+  }
+  // output in ascending index order: mark the chosen indices (all < kRowCap) in a
+  // bitmap; word w's set bits go to slots from the number of bits in words < w
+  for (int w2 = tid; w2 < kRowCap / 32; w2 += kSelThreads) bitmap[w2] = 0u;
+  __syncthreads();
+  for (int i = tid; i < k; i += kSelThreads) atomicOr(&bitmap[chosen[i] >> 5], 1u << (chosen[i] & 31));
+  __syncthreads();
+  constexpr int kWords = kRowCap / 32;  // one word per thread (kWords <= kSelThreads)
+  const uint32_t word = tid < kWords ? bitmap[tid] : 0u;
+  const int cnt = __popc(word);
+  int x = cnt;  // inclusive prefix within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int slot = x - cnt;
+  for (int w2 = 0; w2 < wave; ++w2) slot += wsum[w2];
+  int* orow = out + (size_t)r * K;
+  const int* cmap_row = cand_map ? cand_map + (size_t)r * N : nullptr;
+  for (uint32_t m = word; m; m &= m - 1u) {
+    const int v = 32 * tid + __ffs(m) - 1;
+    orow[slot++] = cmap_row ? cmap_row[v] : v;
+  }
+  for (int i = k + tid; i < K; i += kSelThreads) orow[i] = -1;
 }
 
 hipError_t launch_topk(const float* scores, int R, int N, const int* valid_len, const int* cand_map,
                        int K, int* out_idx, const TopkWs& ws, hipStream_t st) {
   if (R == 0) return hipSuccess;
-  if (N > kTopkCap) {
+  if (N <= kRowCap) {
+    hipLaunchKernelGGL(topk_row_kernel, dim3(R), dim3(kSelThreads), 0, st, scores, N, valid_len,
+                       cand_map, K, out_idx);
+    return hipGetLastError();
+  }
+  {
     hipLaunchKernelGGL(topk_chunkmax_kernel, dim3((2 * K + 3) / 4, R), dim3(256), 0, st, scores, N,
                        valid_len, K, ws.cmax, ws.cnt);
     const int fx = (N + 256 * kFilterPerThread - 1) / (256 * kFilterPerThread);

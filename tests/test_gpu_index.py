@@ -93,7 +93,9 @@ def test_prefill_scores(B, Tq, N, h_i, d_i, m, pos):
 @pytest.mark.parametrize("R,N,K,kind", [(3, 5000, 512, "gauss"), (2, 65536, 512, "gauss"),
                                         (1, 1 << 20, 512, "gauss"), (2, 65536, 512, "ties"),
                                         (4, 8192, 2048, "ties"), (2, 20000, 1, "gauss"),
-                                        (3, 100, 512, "gauss"), (2, 300000, 2048, "gauss")])
+                                        (3, 100, 512, "gauss"), (2, 300000, 2048, "gauss"),
+                                        (64, 12288, 512, "gauss"), (5, 16384, 2048, "gauss"),
+                                        (3, 16384, 512, "ties"), (4, 9000, 1, "gauss")])
 def test_topk_paths(R, N, K, kind):
     rng = np.random.default_rng(N + K)
     if kind == "ties":
