@@ -12,8 +12,8 @@
 // (tiles of H and W staged through LDS), then folds and rotates in registers:
 // each thread owns 4 consecutive tokens (whole blocks for m in {1,2,4}) of one
 // channel pair, so the fold and the pair rotation need no communication.  The
-// result is rounded once to float32.  This path serves cache builds; it is
-// vector fp64 work, not tuned for a timed prefill.
+// result is rounded once to float32.  This path serves float32 inputs and a
+// scalar Z; bf16 inputs take the MFMA kernel below.
 #include "common.h"
 #include "internal.h"
 
@@ -121,11 +121,169 @@ __global__ __launch_bounds__(256) void compress_kernel(const TIn* __restrict__ H
   }
 }
 
+// ---------------------------------------------------------------- bf16 on MFMA
+// For bf16 hidden states and weights (a timed prefill: thousands of tokens at
+// d_model 5,120) the projections run on MFMA with fp32 accumulation.  A
+// workgroup computes 256 tokens x 64 channels of C and the same 64 channels of
+// Z; a wave owns 64 tokens x all 128 columns (its A fragments are reused over
+// 8 column tiles).  H and W pass through LDS in 64-deep slices, double-buffered
+// and fetched one slice ahead; W is transposed on the way in so that every
+// fragment is one 16-byte LDS read.  An MFMA output lane holds 4 consecutive
+// tokens of one channel in C and in Z, so the fold (m in {1,2,4}) needs no
+// communication; the RoPE partner channel sits in the neighbouring lane.
+constexpr int kMT = 256;        // tokens per workgroup
+constexpr int kMC = 64;         // channels of C (and of Z) per workgroup
+constexpr int kMK = 64;         // reduction slice
+constexpr int kMP = kMK + 8;    // LDS pitch (bf16) of a staged H row / W column: 16 B pad
+
+template <int M>
+__global__ __launch_bounds__(256, 1) void compress_mfma_kernel(
+    const uint16_t* __restrict__ H, int T, int d_model, const uint16_t* __restrict__ Wkv,
+    const uint16_t* __restrict__ Wz, int d, long long pos0, int rope_dim, double theta, int n_ent,
+    int n_cg, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t hs[2][kMT * kMP];
+  __shared__ __attribute__((aligned(16))) uint16_t wsm[2][2 * kMC * kMP];
+  // workgroup -> (token group, channel group); the channel groups of one token
+  // group get ids equal mod 8, i.e. one XCD, and share its H slice in that L2
+  const int L = blockIdx.x;
+  const int tg = (L & 7) + 8 * (L / (8 * n_cg));
+  const int cg = (L >> 3) % n_cg;
+  const int b = blockIdx.y;
+  const int T_used = n_ent * M;
+  const int t_base = tg * kMT, c_base = cg * kMC;
+  if (t_base >= T_used) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
+  const uint16_t* Hb = H + (size_t)b * T * d_model;
+
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  // staging: H rows (token) x 8 chunks of 16 B per slice, 8 chunks per thread;
+  // W: thread = (4 reduction rows kq, 8 columns co) of the 64 x 128 slice
+  u32x4 sh[8], sw[4];
+  const int kq = tid & 15, co = tid >> 4;
+  const uint16_t* wsrc = co < 8 ? Wkv + c_base + 8 * co : Wz + c_base + 8 * (co - 8);
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = tid + 256 * u, row = c >> 3, part = c & 7;
+      const int t = min(t_base + row, T_used - 1);
+      sh[u] = *reinterpret_cast<const u32x4*>(Hb + (size_t)t * d_model + k0 + 8 * part);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      sw[r] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)(k0 + 4 * kq + r) * d);
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = tid + 256 * u, row = c >> 3, part = c & 7;
+      *reinterpret_cast<u32x4*>(&hs[buf][row * kMP + 8 * part]) = sh[u];
+    }
+    // column 8co + j gets reduction rows 4kq .. 4kq+3 (8 bytes)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int hi = j & 1, wd = j >> 1;
+      const uint32_t e0 = sw[0][wd], e1 = sw[1][wd], e2 = sw[2][wd], e3 = sw[3][wd];
+      const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+      const u32x2 v = {__builtin_amdgcn_perm(e1, e0, sel), __builtin_amdgcn_perm(e3, e2, sel)};
+      *reinterpret_cast<u32x2*>(&wsm[buf][(8 * co + j) * kMP + 4 * kq]) = v;
+    }
+  };
+
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int n_k = d_model / kMK;
+  fetch(0);
+  stash(0);
+  fetch(min(1, n_k - 1) * kMK);
+  lds_barrier();
+  for (int kc = 0; kc < n_k; ++kc) {
+    const int buf = kc & 1;
+#pragma unroll
+    for (int s = 0; s < kMK / 32; ++s) {
+      bf16x8_t a[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        a[rt] = *reinterpret_cast<const bf16x8_t*>(&hs[buf][(64 * wave + 16 * rt + col) * kMP + 32 * s + 8 * g]);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&wsm[buf][(16 * ct + col) * kMP + 32 * s + 8 * g]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt][ct] = mfma16x16x32(a[rt], bv, acc[rt][ct]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // buffer buf^1 was last read in pass kc-1, before that pass's barrier
+    stash(buf ^ 1);
+    fetch(min(kc + 2, n_k - 1) * kMK);
+    lds_barrier();
+  }
+
+  // ---- fold and RoPE: lane holds tokens t0+i (i = 0..3) of channel c in C and Z
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int t0 = t_base + 64 * wave + 16 * rt + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int c = c_base + 16 * ct + col;
+      const f32x4_t cv = acc[rt][ct], zv = acc[rt][ct + 4];
+#pragma unroll
+      for (int e = 0; e < 4 / M; ++e) {
+        float zmax = zv[e * M];
+#pragma unroll
+        for (int j = 1; j < M; ++j) zmax = fmaxf(zmax, zv[e * M + j]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+          const float a = expf(zv[e * M + j] - zmax);
+          den += a;
+          num = fmaf(a, cv[e * M + j], num);
+        }
+        float kv = num / den;
+        const int ent = (t0 + e * M) / M;
+        if (rope_dim > 0 && c_base + kMC > d - rope_dim) {  // workgroup-uniform
+          const float other = __shfl_xor(kv, 1);
+          if (c >= d - rope_dim) {
+            const int i = (c - (d - rope_dim)) >> 1;
+            const double pos = (double)(pos0 + (long long)(ent + 1) * M - 1);
+            double sn, cs;
+            sincos(pos * pow(theta, -2.0 * i / rope_dim), &sn, &cs);
+            const double u = (c & 1) ? other : kv, v = (c & 1) ? kv : other;
+            kv = (float)((c & 1) ? u * sn + v * cs : u * cs - v * sn);
+          }
+        }
+        if (ent < n_ent) out[((size_t)b * n_ent + ent) * d + c] = kv;
+      }
+    }
+  }
+}
+
+bool compress_mfma_ok(bool bf16_in, int d_model, int d, int d_z) {
+  return bf16_in && d_z == d && d % kMC == 0 && d_model % kMK == 0;
+}
+
 hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_model, const void* W_kv,
                            const void* W_z, int d, int d_z, int m, long long pos0, int rope_dim,
                            double rope_theta, float* kv_out, hipStream_t st) {
   const int n_ent = T / m;
   if (B == 0 || n_ent == 0) return hipSuccess;
+  if (compress_mfma_ok(bf16_in, d_model, d, d_z)) {
+    const int n_tg = (n_ent * m + kMT - 1) / kMT, n_cg = d / kMC;
+    dim3 g2((unsigned)(8 * ((n_tg + 7) / 8) * n_cg), (unsigned)B);
+#define CSA2_COMPM(M_)                                                                                \
+  hipLaunchKernelGGL((compress_mfma_kernel<M_>), g2, dim3(256), 0, st, static_cast<const uint16_t*>(H), \
+                     T, d_model, static_cast<const uint16_t*>(W_kv), static_cast<const uint16_t*>(W_z), d, \
+                     pos0, rope_dim, rope_theta, n_ent, n_cg, kv_out)
+    if (m == 1) CSA2_COMPM(1);
+    else if (m == 2) CSA2_COMPM(2);
+    else CSA2_COMPM(4);
+#undef CSA2_COMPM
+    return hipGetLastError();
+  }
   dim3 grid((d + kCC - 1) / kCC, (n_ent * m + kCT - 1) / kCT, B);
 #define CSA2_COMP(TIN, M_)                                                                          \
   hipLaunchKernelGGL((compress_kernel<TIN, M_>), grid, dim3(256), 0, st, static_cast<const TIN*>(H), \

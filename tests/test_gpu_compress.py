@@ -1,5 +1,6 @@
-"""GPU parity: compressor (projections, softmax fold, RoPE).  Bar: 1e-4 x RMS; the
-kernel sums in float64, so it also agrees with the oracle to float32 rounding."""
+"""GPU parity: compressor (projections, softmax fold, RoPE).  Bar: 1e-4 x RMS.  Float32
+inputs (and a scalar Z) take the float64 kernel, which also agrees with the oracle to
+float32 rounding; bf16 inputs take the MFMA kernel (fp32 accumulation)."""
 import numpy as np
 import pytest
 import torch
@@ -22,6 +23,11 @@ def bd():
     (1, 130, 80, 128, 1, 4, 24576, 64, False),
     (1, 96, 64, 512, 512, 2, 24576, 64, True),
     (1, 40, 32, 64, 64, 2, 0, 0, False),
+    (2, 600, 128, 256, 256, 1, 0, 64, True),
+    (1, 300, 192, 128, 128, 4, 8, 64, True),
+    (1, 1030, 320, 512, 512, 2, 24576, 64, True),
+    (1, 200, 128, 128, 1, 2, 0, 64, True),
+    (1, 64, 64, 64, 64, 1, 3, 0, True),
 ])
 def test_compress(B, T, dm, d, dz, m, pos0, r, bf16):
     rng = np.random.default_rng(T + d)
@@ -39,6 +45,7 @@ def test_compress(B, T, dm, d, dz, m, pos0, r, bf16):
         rms = np.sqrt(np.mean(ref ** 2))
         assert out.shape[1] == T // m
         assert np.max(np.abs(out[b] - ref)) <= 1e-4 * rms
-        # float64 sums: within a float32 rounding of the oracle almost everywhere
-        close = np.abs(out[b] - ref) <= np.abs(ref) * 2.0 ** -23 + 1e-30
-        assert close.mean() > 0.999
+        if not bf16 or dz == 1:
+            # float64 sums: within a float32 rounding of the oracle almost everywhere
+            close = np.abs(out[b] - ref) <= np.abs(ref) * 2.0 ** -23 + 1e-30
+            assert close.mean() > 0.999
