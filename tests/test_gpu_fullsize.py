@@ -1,0 +1,79 @@
+"""GPU parity at the full decode sizes, in the benchmark's launch configuration.
+
+The cache and per-layer inputs are built exactly as ``bench.py`` builds them and one
+decode step is replayed from a captured graph.  The outputs are then checked on
+sampled sequences (the first and the last), stage by stage, each oracle stage
+consuming the GPU's previous output:
+  * FP4 codes / scales and indexer keys of a sampled range of entries, against the
+    oracle's quantisation of the regenerated float32 entries (bit-exact);
+  * the Full layer's Top-K against the oracle's scores of every entry (near-tie
+    exemption), the shared pool against the oracle's pool of the GPU's scores
+    (exact), each Reindex layer's Top-K against the oracle's rescoring of the pool;
+  * attention of sampled layers within 2e-3 x RMS of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import attn_close, check_topk, host_bf16_bits
+from oracle.csa2 import (build_pool, index_scores, indexer_k, quant_fp4, sparse_attention)
+
+pytestmark = pytest.mark.gpu
+
+
+def mods():
+    import bench
+    from kv_cache_compression_03_amd import binding, schedule
+    return bench, binding, schedule
+
+
+@pytest.mark.parametrize("name,attn_layers", [
+    ("decode_64k_b64", [0, 1, 2, 3]),
+    ("reindex_256k_b32", [0, 1, 2, 3]),
+    ("decode_1m_b8", [0, 3, 4, 11, 19]),
+])
+def test_decode_full_size_sampled(name, attn_layers):
+    bench, bd, sch = mods()
+    wl = synth.workload(name)
+    print(f"[fullsize] {name}: B={wl.B} N={wl.N} schedule={wl.schedule}", flush=True)
+    codes, scales, kidx, layers = bench.build_inputs(wl, torch, bd, sch)
+    run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
+                             G=wl.G, PB=wl.PB, PE=wl.PE)
+    g = run.capture(codes, scales, kidx, layers)
+    g.replay()
+    torch.cuda.synchronize()
+    W = synth.w_ik(wl)
+    for b in sorted({0, wl.B - 1}):
+        # FP4 codes / scales / indexer keys of a sampled range (every stored byte of it)
+        lo = (7919 * (b + 1)) % max(1, wl.N - 4096)
+        hi = min(wl.N, lo + 4096)
+        q8 = quant_fp4(synth.main_kv(wl, b, lo, hi))
+        c_b, s_b = codes[b].cpu().numpy(), scales[b].cpu().numpy()
+        k_b = host_bf16_bits(kidx[b])
+        assert np.array_equal(c_b[lo:hi], q8.codes) and np.array_equal(s_b[lo:hi], q8.scales)
+        assert np.array_equal(k_b[lo:hi], indexer_k(q8.codes, q8.scales, W))
+        pool = None
+        if run.need_pool:
+            pool = run.pool[b, :run.pool_len[b].item()].cpu().numpy()
+            gsc = run.scores[b, 0].cpu().numpy().astype(np.float64)
+            assert np.array_equal(pool, build_pool(gsc, wl.G, wl.PB, wl.PE))
+            assert pool.shape[0] == wl.PB * wl.PE  # 2,048 blocks x 8 entries
+        sel_prev = None
+        for li, mode in enumerate(wl.layers):
+            gsel = run.selection_of(li)[b, 0].cpu().numpy()
+            qi = synth.q_index(wl, li, b)[0] if mode in "FR" else None
+            w = synth.head_weights(wl, li, b)[0] if mode in "FR" else None
+            if mode == "F":
+                check_topk(gsel, index_scores(qi, w, k_b), wl.K)
+            elif mode == "R":
+                check_topk(gsel, index_scores(qi, w, k_b[pool]), wl.K, index_map=pool)
+            else:
+                assert np.array_equal(gsel, sel_prev)
+            sel_prev = gsel
+            if li in attn_layers:
+                out = run.out[li][b, 0].cpu().numpy()
+                ref = sparse_attention(synth.q_main(wl, li, b)[0], c_b, s_b, gsel,
+                                       synth.swa_tokens(wl, li, b))
+                attn_close(out, ref)
+        print(f"[fullsize] {name}: sequence {b} checked", flush=True)
