@@ -75,7 +75,9 @@ CSA2_API const char* csa2_last_error(void);
  *   W_kv   [d_model, d]     f32 or bf16 (w_dtype, must equal h_dtype)
  *   W_z    [d_model, d_z]   d_z = d (per-channel weights) or 1 (one per token)
  *   kv_out [B, T/m, d]      f32 (T/m rounded down)
- * Sums run in float64; the result is rounded once to float32.
+ * Float32 inputs (or d_z = 1): sums in float64, the result rounded once to
+ * float32.  Bf16 inputs with d_z = d and d_model % 64 == 0: the projections run
+ * on MFMA, exact bf16 products summed in float32.
  * Limits: m in {1,2,4}, d % 64 == 0, rope_dim even and <= d, pos0 % m == 0.
  */
 CSA2_API int csa2_compress(const void* H, int h_dtype, int B, int T, int d_model,
@@ -131,7 +133,7 @@ CSA2_API int csa2_index_full(const void* q_idx, const float* w, const void* k_id
  *   cand_map  [R, N] int32 or NULL: output cand_map[r][i] instead of i; each row
  *             must be ascending (so index order is kept), e.g. a candidate pool
  *   out_idx   [R, K] int32
- *   ws        >= csa2_topk_workspace(R, N, K) bytes
+ *   ws        >= csa2_topk_workspace(R, N, K) bytes (0 when N <= 16384)
  * Limits: 1 <= K <= 2048.  Scores must not be NaN.
  */
 CSA2_API size_t csa2_topk_workspace(int R, int N, int K);
