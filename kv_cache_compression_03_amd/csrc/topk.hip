@@ -112,8 +112,13 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restric
   __shared__ float red[4];
   __shared__ int wsum[4];
   __shared__ int base;
+  // C <= 2K <= 4096 chunk maxima: every load of a thread issued at once
   float mn = INFINITY;
-  for (int c = tid; c < C; c += 256) mn = fminf(mn, cmax[(size_t)r * 2 * K + c]);
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int c = tid + 256 * u;
+    if (c < C) mn = fminf(mn, cmax[(size_t)r * 2 * K + c]);
+  }
   mn = wave_min(mn);
   if (lane == 0) red[wave] = mn;
   __syncthreads();
@@ -357,10 +362,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     for (int i = tid; i < k; i += kSelThreads) chosen[i] = sel[i];
     __syncthreads();
   } else {
-    for (int i = tid; i < total; i += kSelThreads) {
-      const float s = direct ? row[i] : cscore[(size_t)r * kTopkCap + i];
-      const int idx = direct ? i : cidx[(size_t)r * kTopkCap + i];
-      keys[i] = make_key(s, idx);
+    // all of a thread's loads first, then the LDS writes (one memory round trip)
+    constexpr int kPer = kTopkCap / kSelThreads;
+    float sv[kPer];
+    int iv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kSelThreads;
+      sv[u] = i < total ? (direct ? row[i] : cscore[(size_t)r * kTopkCap + i]) : 0.0f;
+      iv[u] = i < total ? (direct ? i : cidx[(size_t)r * kTopkCap + i]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kSelThreads;
+      if (i < total) keys[i] = make_key(sv[u], iv[u]);
     }
     if (tid == 0) misc[0] = 0;
     __syncthreads();
@@ -401,11 +416,28 @@ __global__ __launch_bounds__(kSelThreads) void topk_row_kernel(
   const int k = min(K, n);
   const float* row = scores + (size_t)r * N;
   int total;
+  // every load of a thread is issued before its first LDS write, so the row
+  // arrives in one memory round trip rather than one per element
+  constexpr int kPer = kRowCap / kSelThreads;
+  float rv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * kSelThreads;
+    rv[u] = i < n ? row[i] : 0.0f;
+  }
   if (n <= kTopkCap) {
-    for (int i = tid; i < n; i += kSelThreads) keys[i] = make_key(row[i], i);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kSelThreads;
+      if (i < n) keys[i] = make_key(rv[u], i);
+    }
     total = n;
   } else {
-    for (int i = tid; i < n; i += kSelThreads) s_row[i] = row[i];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kSelThreads;
+      if (i < n) s_row[i] = rv[u];
+    }
     if (tid == 0) misc[0] = 0;
     __syncthreads();
     // C >= K chunks of clen entries: their maxima are C distinct entries, so the
