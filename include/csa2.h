@@ -174,6 +174,12 @@ CSA2_API int csa2_index_reindex(const void* q_idx, const float* w, const void* k
  *   sm_scale <= 0 selects 1/sqrt(d).
  *   ws     >= csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) bytes
  * Limits: d in {256, 512}, H_q % 16 == 0, K <= 2048.
+ * Precision: products are exact (entries, window values and probabilities are
+ * carried in fp16 or bf16, both exact for the decoded values) and accumulate in
+ * fp32.  When H_q % 32 == 0, |swa_scale| <= 128 and codes, scales and swa are
+ * 16-byte aligned, the fp16 kernel runs (probabilities with 11 significant bits,
+ * queries scaled into fp16 by a power of two per head); otherwise the bf16
+ * kernel (probabilities as a bf16 pair, 16 bits).
  */
 CSA2_API size_t csa2_sparse_attn_workspace(int B, int Tq, int H_q, int d, int K, int S);
 CSA2_API int csa2_sparse_attn(const void* q, const uint8_t* codes, const uint8_t* scales, int N,

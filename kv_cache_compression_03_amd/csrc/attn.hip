@@ -32,14 +32,12 @@
 //     cross-lane traffic on the common path); per-split
 //     (O, m, l) partials are merged by a small combine kernel (or written
 //     directly when there is one split).
+#include "attn_common.h"
 #include "common.h"
 #include "internal.h"
 
 namespace csa2 {
 
-constexpr int kKC = 32;  // keys per chunk
-constexpr int kMaxSplits = 64;  // key splits a row may be cut into
-constexpr int kMaxSel = 2048;   // selection slots a row may hold (all staged in LDS)
 #ifndef CSA2_ATTN_TARGET_WGS
 #define CSA2_ATTN_TARGET_WGS 256  // workgroups a launch aims for (splits = target / rows)
 #endif
@@ -78,31 +76,6 @@ size_t attn_ws_bytes(int B, int Tq, int H_q, int d, int K, int L_max) {
   return align256(rows * p.n_splits * H_q * d * sizeof(float)) +
          align256(rows * p.n_splits * H_q * 2 * sizeof(float));
 }
-
-// Workgroups are dispatched to the 8 XCDs round-robin by id, and each XCD has its
-// own L2.  With >= 8 rows, all workgroups of a row (its key splits and head
-// groups) are placed on one XCD, so the row's queries and partial results are
-// shared through that L2.  Returns false for the padding ids of the last round.
-CSA2_DEV bool xcd_map(int id, int rows, int per_row, int& row, int& unit) {
-  if (rows < 8) {
-    row = id / per_row;
-    unit = id - row * per_row;
-    return row < rows;
-  }
-  const int x = id & 7, k = id >> 3;
-  const int lr = k / per_row;
-  unit = k - lr * per_row;
-  row = lr * 8 + x;
-  return row < rows;
-}
-static inline int xcd_grid(int rows, int per_row) {
-  return rows < 8 ? rows * per_row : 8 * ((rows + 7) / 8) * per_row;
-}
-
-// Softmax state is kept against a reference maximum that only moves when a new
-// logit exceeds it by more than 2^kLazy (log2 units), so O is rarely rescaled;
-// probabilities stay below 2^kLazy, far inside float range.
-constexpr float kLazy = 8.0f;
 
 template <int D, int HG>
 __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
@@ -465,22 +438,31 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
                                        align256((size_t)rows * p.n_splits * H_q * d * sizeof(float)));
   }
   const float sm_log2 = sm_scale * 1.4426950408889634f;
-  dim3 grid(xcd_grid(rows, p.n_splits * p.head_groups));
-  const int hg = p.waves / 2;
-#define CSA2_ATTN(D_, HG_)                                                                          \
-  hipLaunchKernelGGL((sparse_attn_kernel<D_, HG_>), grid, dim3(HG_ * 2 * 64), 0, st, q, codes, scales, \
-                     N, sel, K, swa, swa_scale, S, swa_pos0, n_win, q_pos, Tq, H_q, sm_log2,          \
-                     p.chunks_per_split, p.n_splits, rows, p.head_groups, part_o, part_ml, out, lse)
-  if (d == 512) {
-    if (hg == 4) CSA2_ATTN(512, 4);
-    else if (hg == 2) CSA2_ATTN(512, 2);
-    else CSA2_ATTN(512, 1);
+  const bool aligned = ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(scales) |
+                         reinterpret_cast<uintptr_t>(swa)) & 15) == 0;
+  if (aligned && attn_f16_supported(H_q, d, swa_scale)) {
+    hipError_t e = launch_sparse_attn_f16(q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0,
+                                          n_win, q_pos, Tq, H_q, d, sm_log2, p, rows, part_o, part_ml,
+                                          out, lse, st);
+    if (e != hipSuccess) return e;
   } else {
-    if (hg == 4) CSA2_ATTN(256, 4);
-    else if (hg == 2) CSA2_ATTN(256, 2);
-    else CSA2_ATTN(256, 1);
-  }
+    dim3 grid(xcd_grid(rows, p.n_splits * p.head_groups));
+    const int hg = p.waves / 2;
+  #define CSA2_ATTN(D_, HG_)                                                                          \
+    hipLaunchKernelGGL((sparse_attn_kernel<D_, HG_>), grid, dim3(HG_ * 2 * 64), 0, st, q, codes, scales, \
+                       N, sel, K, swa, swa_scale, S, swa_pos0, n_win, q_pos, Tq, H_q, sm_log2,          \
+                       p.chunks_per_split, p.n_splits, rows, p.head_groups, part_o, part_ml, out, lse)
+    if (d == 512) {
+      if (hg == 4) CSA2_ATTN(512, 4);
+      else if (hg == 2) CSA2_ATTN(512, 2);
+      else CSA2_ATTN(512, 1);
+    } else {
+      if (hg == 4) CSA2_ATTN(256, 4);
+      else if (hg == 2) CSA2_ATTN(256, 2);
+      else CSA2_ATTN(256, 1);
+    }
 #undef CSA2_ATTN
+  }
   if (p.n_splits > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3(xcd_grid(rows, H_q)), dim3(128), 0, st, part_o,
                        part_ml, p.n_splits, H_q, d, rows, out, lse);

@@ -1,0 +1,49 @@
+// Pieces shared by the two sparse-attention kernels (attn.hip, attn_f16.hip).
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+
+constexpr int kKC = 32;         // keys per chunk
+constexpr int kMaxSplits = 64;  // key splits a row may be cut into
+constexpr int kMaxSel = 2048;   // selection slots a row may hold (all staged in LDS)
+
+// Softmax state is kept against a reference maximum that only moves when a new
+// logit exceeds it by more than 2^kLazy (log2 units), so O is rarely rescaled;
+// probabilities stay below 2^kLazy, far inside float range.
+constexpr float kLazy = 8.0f;
+
+// Workgroups are dispatched to the 8 XCDs round-robin by id, and each XCD has its
+// own L2.  With >= 8 rows, all workgroups of a row (its key splits and head
+// groups) are placed on one XCD, so the row's queries and partial results are
+// shared through that L2.  Returns false for the padding ids of the last round.
+CSA2_DEV bool xcd_map(int id, int rows, int per_row, int& row, int& unit) {
+  if (rows < 8) {
+    row = id / per_row;
+    unit = id - row * per_row;
+    return row < rows;
+  }
+  const int x = id & 7, k = id >> 3;
+  const int lr = k / per_row;
+  unit = k - lr * per_row;
+  row = lr * 8 + x;
+  return row < rows;
+}
+static inline int xcd_grid(int rows, int per_row) {
+  return rows < 8 ? rows * per_row : 8 * ((rows + 7) / 8) * per_row;
+}
+
+// fp16 kernel (attn_f16.hip): 32-head groups, whole selection of a split staged.
+// Usable when H_q is a multiple of 32, d is 256 or 512 and |swa_scale| <= 128 (so
+// that probabilities times the window scale stay inside fp16 range).
+bool attn_f16_supported(int H_q, int d, float swa_scale);
+hipError_t launch_sparse_attn_f16(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                  int N, const int* sel, int K, const uint8_t* swa, float swa_scale,
+                                  int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,
+                                  int H_q, int d, float sm_log2, const AttnPlan& p, int rows,
+                                  float* part_o, float* part_ml, float* out, float* lse,
+                                  hipStream_t st);
+
+}  // namespace csa2

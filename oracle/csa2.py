@@ -342,6 +342,19 @@ def attend(q, keys, sm_scale: Optional[float] = None) -> np.ndarray:
     return p @ k
 
 
+def attend_lse(q, keys, sm_scale: Optional[float] = None) -> np.ndarray:
+    """Natural-log normaliser of attend()'s softmax per head:
+    log sum_j exp(q_h · key_j * sm_scale).  No keys -> -inf.  float64 [H_q]."""
+    qf = _as_f64(q)
+    k = np.asarray(keys, dtype=np.float64)
+    if k.shape[0] == 0:
+        return np.full(qf.shape[0], -np.inf)
+    sc = 1.0 / np.sqrt(qf.shape[-1]) if sm_scale is None else float(sm_scale)
+    lg = qf @ k.T * sc
+    mx = lg.max(axis=1)
+    return mx + np.log(np.exp(lg - mx[:, None]).sum(axis=1))
+
+
 def swa_window_rows(q_pos: Optional[int], S: int, swa_pos0: int, n_win: int) -> np.ndarray:
     """R14: the window is the n_win most recent tokens including the query's
     own: positions (t - n_win, t].  A decode query (q_pos None) sees the whole

@@ -1,5 +1,9 @@
 """GPU parity: sparse attention over selected FP4 entries ++ the FP8 window.
-Bar: max |gpu - oracle| <= 2e-3 x RMS(oracle output) (fp32 accumulation)."""
+Bar: max |gpu - oracle| <= 2e-3 x RMS(oracle output) (fp32 accumulation); the
+log-sum-exp within 2e-4 x (1 + |oracle|).
+
+Shapes with H_q a multiple of 32 (and |swa_scale| <= 128) run the fp16 kernel,
+the others the bf16 kernel; both are covered here."""
 import numpy as np
 import pytest
 import torch
@@ -7,7 +11,8 @@ import torch
 import synth
 from helpers import dev, dev_bf16
 from oracle.codecs import f64_to_bf16
-from oracle.csa2 import quant_fp4, sparse_attention
+from oracle.csa2 import (attend_lse, attention_keys, quant_fp4, sparse_attention,
+                         swa_window_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +44,15 @@ def compare(out, ref):
     return err / rms
 
 
+def compare_lse(lse, q, codes, scales, sel, swa, swa_scale=1.0, q_pos=None, swa_pos0=0, n_win=128):
+    rows = swa_window_rows(q_pos, swa.shape[0], swa_pos0, n_win)
+    ref = attend_lse(q, attention_keys(codes, scales, sel, swa, swa_scale, rows))
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.all(np.abs(lse[fin] - ref[fin]) <= 2e-4 * (1 + np.abs(ref[fin]))), \
+        np.max(np.abs(lse[fin] - ref[fin]))
+
+
 @pytest.mark.parametrize("B,H,d,N,K,S,n_sel", [
     (2, 16, 256, 2048, 512, 128, None),     # one-layer decode at 4K, m = 2
     (3, 64, 512, 5000, 512, 128, None),     # decode
@@ -47,6 +61,10 @@ def compare(out, ref):
     (2, 32, 512, 1000, 512, 128, 0),        # empty selection: window only
     (2, 64, 512, 4000, 512, 128, 77),       # ragged selection
     (9, 64, 512, 3000, 512, 128, None),     # more rows (different split plan)
+    (2, 64, 256, 2048, 512, 128, None),     # d = 256, two 32-head groups per workgroup
+    (2, 32, 256, 2048, 300, 77, None),      # d = 256, one 32-head group, ragged window
+    (2, 96, 512, 3000, 512, 128, None),     # three 32-head workgroups per split
+    (2, 48, 512, 3000, 512, 128, None),     # H_q not a multiple of 32: bf16 kernel
 ])
 def test_decode_attention(B, H, d, N, K, S, n_sel):
     rng = np.random.default_rng(N + H + d)
@@ -59,18 +77,42 @@ def test_decode_attention(B, H, d, N, K, S, n_sel):
     ref = np.stack([sparse_attention(q[b, 0], codes[b], scales[b], sel[b, 0], swa[b])
                     for b in range(B)])
     compare(out[:, 0], ref)
+    for b in range(B):
+        compare_lse(lse[b, 0], q[b, 0], codes[b], scales[b], sel[b, 0], swa[b])
 
 
-def test_swa_scale_and_prefill_positions():
+@pytest.mark.parametrize("q_exp", [-60, 60])
+def test_query_magnitudes(q_exp):
+    """Queries far from unit scale (flat and one-hot attention): the fp16 kernel
+    moves each head into fp16 range by a power of two."""
+    rng = np.random.default_rng(100 + q_exp)
+    B, H, d, N, K, S = 2, 64, 512, 3000, 512, 128
+    codes, scales, q, sel, swa = make_case(rng, B, 1, H, d, N, K, S)
+    q = f64_to_bf16(rng.standard_normal((B, 1, H, d)) * 2.0 ** q_exp)
+    lse = torch.empty(B, 1, H, dtype=torch.float32, device="cuda")
+    out = bd().csa2_sparse_attn(dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa),
+                                swa_scale=1.0, lse=lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        compare(out[b, 0], sparse_attention(q[b, 0], codes[b], scales[b], sel[b, 0], swa[b]))
+        compare_lse(lse[b, 0], q[b, 0], codes[b], scales[b], sel[b, 0], swa[b])
+
+
+@pytest.mark.parametrize("swa_scale", [0.37, 100.0, 200.0])   # 200: above the fp16 kernel's limit
+def test_swa_scale_and_prefill_positions(swa_scale):
     rng = np.random.default_rng(11)
     B, Tq, H, d, N, K, S, n_win = 1, 7, 32, 512, 4000, 64, 300, 128
     codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S)
     swa_pos0 = 1000
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device="cuda")
     pos = np.array([[999, 1000, 1050, 1127, 1128, 1299, 1400]], np.int32)   # window edges
     out = bd().csa2_sparse_attn(dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa),
-                                swa_scale=0.37, q_pos=dev(pos), swa_pos0=swa_pos0, n_win=n_win)
-    out = out.cpu().numpy()
+                                swa_scale=swa_scale, q_pos=dev(pos), swa_pos0=swa_pos0, n_win=n_win,
+                                lse=lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
     for t in range(Tq):
-        ref = sparse_attention(q[0, t], codes[0], scales[0], sel[0, t], swa[0], 0.37,
+        ref = sparse_attention(q[0, t], codes[0], scales[0], sel[0, t], swa[0], swa_scale,
                                q_pos=int(pos[0, t]), swa_pos0=swa_pos0, n_win=n_win)
         compare(out[0, t], ref)
+        compare_lse(lse[0, t], q[0, t], codes[0], scales[0], sel[0, t], swa[0], swa_scale,
+                    q_pos=int(pos[0, t]), swa_pos0=swa_pos0, n_win=n_win)

@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 from oracle.codecs import e4m3_decode
-from oracle.csa2 import (attend, dequant_fp4, quant_fp4, sparse_attention, swa_window_rows)
+from oracle.csa2 import (attend, attend_lse, dequant_fp4, quant_fp4, sparse_attention, swa_window_rows)
 
 rng = np.random.default_rng(4)
 
@@ -77,3 +77,23 @@ def test_attend_uses_given_scale():
     k = rng.standard_normal((7, 16))
     q = rng.standard_normal((2, 16))
     assert np.allclose(attend(q, k, 0.3), _sdpa(q, k, 0.3), atol=1e-13)
+
+
+def test_attend_lse_special_cases():
+    """log-sum-exp pins: n copies of one key give logit + log n; a single key gives
+    its logit; no keys give -inf; shifting every logit by c shifts lse by c."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 8))
+    k1 = rng.standard_normal((1, 8))
+    lg = q @ k1[0] / np.sqrt(8)
+    assert np.allclose(attend_lse(q, k1), lg, atol=1e-13)
+    assert np.allclose(attend_lse(q, np.repeat(k1, 5, axis=0)), lg + np.log(5), atol=1e-13)
+    assert np.all(attend_lse(q, np.zeros((0, 8))) == -np.inf)
+    k = rng.standard_normal((7, 8))
+    # a key component along q adds q·u * sc to every logit of that head
+    u = np.zeros(8); u[0] = 1.0
+    q0 = np.zeros((1, 8)); q0[0, 0] = 2.0
+    shift = attend_lse(q0, k + 3.0 * u) - attend_lse(q0, k)
+    assert np.allclose(shift, 2.0 * 3.0 / np.sqrt(8), atol=1e-12)
+    # large logits do not overflow (max-shifted evaluation)
+    assert np.isfinite(attend_lse(q * 1e4, k)).all()
