@@ -71,9 +71,11 @@ CSA2_DEV uint32_t fp8x2_f16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
-// Byte offset of key row k in a chunk buffer whose plain row stride is KSTB.
-template <int KSTB>
-CSA2_DEV int row_off_t(int k) { return k * KSTB + 16 * (4 * (k & 3) + ((k >> 2) & 3)); }
+// Key held by MFMA row m of a 32-key chunk: inside each 16-key half the 4x4
+// grid (m/4, m%4) is transposed.  Any order works as long as K rows, the
+// validity mask and the V slots agree; this one makes the four keys of each
+// transposing V read sit 4 rows apart.
+CSA2_DEV int key_of_row(int m) { return (m & 16) | ((m & 3) << 2) | ((m >> 2) & 3); }
 
 template <int D, int HG2>
 __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
@@ -86,22 +88,22 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   constexpr int DS = 4;              // dim quarters
   constexpr int NW = DS * HG2, NT = 64 * NW;
   constexpr int DH = D / DS;         // dims per wave
-  constexpr int KSTB = 2 * D + 256;  // bytes per key row in LDS (room for the row shift)
+  constexpr int KSTB = 2 * D + 16;   // bytes per key row in LDS
   constexpr int VPT = kKC * D / NT;  // values each thread decodes per chunk
   constexpr int NU = VPT / 8;        // 16-byte LDS units each thread writes per chunk
   constexpr int NSB = VPT / 16;      // E4M3 block scales per thread
   static_assert(VPT >= 16 && VPT % 16 == 0 && DH % 32 == 0, "decode split");
-  // Key row k starts at k*KSTB + 16*(4*(k%4) + (k/4)%4) bytes.  Sixteen
-  // consecutive keys then start in 16 distinct 16-byte bank slots (decode writes
-  // and S^T operand reads: one column of 16 keys per instruction), and the four
-  // keys of an aligned quad 64 bytes apart (transposing V reads: 64 contiguous
-  // bytes of each of 4 keys) - no bank conflicts - while every per-step offset
-  // stays a compile-time immediate, so each lane needs one base address per role.
-  __shared__ __attribute__((aligned(16))) uint8_t kv[2][kKC * KSTB];
+  // Key row k starts at k*KSTB bytes, i.e. in 16-byte bank slot k mod 16.  The
+  // decode writes and the S^T operand reads touch one column of 16 keys per
+  // instruction (16 distinct slots); with the row order of key_of_row() each
+  // transposing V read touches 64 contiguous bytes of 4 keys whose slots are 4
+  // apart.  No bank conflicts, and every per-step offset is a compile-time
+  // immediate.  Three chunk buffers: chunk c is multiplied while c+1 is being
+  // multiplied too (S^T) and c+2 is decoded.
+  __shared__ __attribute__((aligned(16))) uint8_t kv[3][kKC * KSTB];
   __shared__ __attribute__((aligned(16))) float sx[NW * 4 * 64 * 4];     // partial logit tiles
   __shared__ __attribute__((aligned(16))) float sfin[HG2 * 4 * 64 * 4];  // summed tiles
   __shared__ int s_ent[kMaxSel];  // entry of each selection slot this split reads
-  auto row_off = [](int k) { return row_off_t<KSTB>(k); };
 
   int row, split;
   if (!xcd_map(blockIdx.x, rows, n_splits * head_groups, row, split)) return;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   };
   // ---- decode the raw registers into one LDS buffer (exact fp16)
   auto decode = [&](uint8_t* buf, bool main_chunk) {
-    uint8_t* rp = buf + row_off(dkey) + dseg * NU * 16;
+    uint8_t* rp = buf + dkey * KSTB + dseg * NU * 16;
     if (main_chunk) {
       // this thread's scale bytes: offset (dseg*NSB) mod 16 of slot NCL
       const int so = (dseg * NSB) & 15;
@@ -249,74 +251,80 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   for (int n = 0; n < DH / 32; ++n) o[n] = f32x16_t{};
   float m_ref = -INFINITY, l_run = 0.0f;
 
-  // S^T operand: key hl, dims dim0 + 16s + 8hh (+32 bytes per step s)
-  const int qk_off = row_off(hl) + ((dim0 >> 3) + hh) * 16;
-  // transposing V reads: as a source lane, this lane addresses key 16t + vk
-  // (+8 for the second read) and dims dim0 + 32n + vd .. +3
-  const int vk = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  // S^T operand: MFMA row hl = key key_of_row(hl), dims dim0 + 16s + 8hh
+  // (+32 bytes per step s)
+  const int qk_off = key_of_row(hl) * KSTB + ((dim0 >> 3) + hh) * 16;
+  // transposing V reads, k-step t, slots 0-3 / 4-7 = MFMA rows 16t + 4hh + e /
+  // 16t + 8 + 4hh + e = keys 16t + 4e + hh / 16t + 4e + hh + 2; as a source lane
+  // this lane addresses e = (lane%16)/4 and dims dim0 + 32n + vd .. +3
   const int vd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int pv_off = row_off(vk) + ((dim0 + vd) >> 3) * 16 + (((vd >> 2) & 1) << 3);
+  const int pv_off = (4 * ((lane & 15) >> 2) + hh) * KSTB + ((dim0 + vd) >> 3) * 16 + (((vd >> 2) & 1) << 3);
 
+  auto qk = [&](const uint8_t* kb) {
+    f32x16_t st = f32x16_t{};
+    const uint8_t* kr = kb + qk_off;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s)
+      st = mfma32x32x16_f16(*reinterpret_cast<const f16x8_t*>(kr + 32 * s), qh[s], st);
+    return st;
+  };
+  // The head group's four partial logit tiles: each wave adds one quarter of the
+  // tile (in dim-quarter order) and every wave reads the finished tile.  The
+  // first barrier also orders everything before it against what follows (buffer
+  // reuse), the second publishes the sum.
+  auto exchange = [&](f32x16_t st) {
+    float4* mine = reinterpret_cast<float4*>(sx + wave * 1024);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      mine[r * 64 + lane] = make_float4(st[4 * r] * qs, st[4 * r + 1] * qs, st[4 * r + 2] * qs,
+                                        st[4 * r + 3] * qs);
+    lds_barrier();
+    const int hg = wave % HG2;
+    const float4* grp = reinterpret_cast<const float4*>(sx + hg * 1024) + dq * 64 + lane;
+    const float4 a0 = grp[0], a1 = grp[HG2 * 256], a2 = grp[2 * HG2 * 256], a3 = grp[3 * HG2 * 256];
+    reinterpret_cast<float4*>(sfin + hg * 1024)[dq * 64 + lane] =
+        make_float4((a0.x + a1.x) + (a2.x + a3.x), (a0.y + a1.y) + (a2.y + a3.y),
+                    (a0.z + a1.z) + (a2.z + a3.z), (a0.w + a1.w) + (a2.w + a3.w));
+    lds_barrier();
+    const float4* fin = reinterpret_cast<const float4*>(sfin + hg * 1024);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 v = fin[r * 64 + lane];
+      st[4 * r] = v.x;
+      st[4 * r + 1] = v.y;
+      st[4 * r + 2] = v.z;
+      st[4 * r + 3] = v.w;
+    }
+    return st;
+  };
+
+  // ---- prologue: chunks c_begin and c_begin+1 decoded, c_begin+2 in flight,
+  // the logits of c_begin summed
+  f32x16_t st = f32x16_t{};
   if (c_begin < c_end) {
     decode(kv[0], c_begin < nm);
-    if (c_begin + 1 < c_end) load_raw(c_begin + 1);
+    if (c_begin + 1 < c_end) {
+      load_raw(c_begin + 1);
+      decode(kv[1], c_begin + 1 < nm);
+      if (c_begin + 2 < c_end) load_raw(c_begin + 2);
+    }
+    lds_barrier();
+    st = exchange(qk(kv[0]));
   }
-  lds_barrier();
   for (int c = c_begin; c < c_end; ++c) {
-    const int buf = (c - c_begin) & 1;
+    const int buf = (c - c_begin) % 3;
     const bool main_chunk = c < nm;
-    const uint8_t* kb = kv[buf];
+    // ---- S^T of the next chunk (its result is only needed after this chunk's
+    // softmax and P·V, so the MFMAs overlap them); past the last chunk it reads
+    // a stale buffer and is discarded
+    const f32x16_t stn = qk(kv[buf == 2 ? 0 : buf + 1]);
 
-    // ---- S^T = K·Q^T over this wave's dims
-    f32x16_t st = f32x16_t{};
-    {
-      const uint8_t* kr = kb + qk_off;
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s)
-        st = mfma32x32x16_f16(*reinterpret_cast<const f16x8_t*>(kr + 32 * s), qh[s], st);
-    }
-    // ---- which keys of the chunk are real (selection slots that hold an entry,
-    // window rows inside the window)
-    uint32_t vmask;
-    if (main_chunk) {
-      vmask = (uint32_t)__ballot(s_ent[c * kKC + hl - sl_lo] >= 0);
-    } else {
-      const int nv = n_swa - (c - nm) * kKC;
-      vmask = nv >= kKC ? 0xFFFFFFFFu : ((1u << nv) - 1u);
-    }
-    // ---- the head group's four partial logit tiles: each wave adds one quarter
-    // of the tile (in dim-quarter order) and every wave reads the finished tile.
-    // Barrier 1 also means every wave is done with the other buffer (chunk c-1),
-    // so chunk c+1 is decoded into it now; barrier 2 publishes it.
-    {
-      float4* mine = reinterpret_cast<float4*>(sx + wave * 1024);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        mine[r * 64 + lane] = make_float4(st[4 * r] * qs, st[4 * r + 1] * qs, st[4 * r + 2] * qs,
-                                          st[4 * r + 3] * qs);
-      lds_barrier();
-      if (c + 1 < c_end) {
-        decode(kv[buf ^ 1], c + 1 < nm);
-        if (c + 2 < c_end) load_raw(c + 2);
-      }
-      const int hg = wave % HG2;
-      const float4* grp = reinterpret_cast<const float4*>(sx + hg * 1024) + dq * 64 + lane;
-      const float4 a0 = grp[0], a1 = grp[HG2 * 256], a2 = grp[2 * HG2 * 256], a3 = grp[3 * HG2 * 256];
-      reinterpret_cast<float4*>(sfin + hg * 1024)[dq * 64 + lane] =
-          make_float4((a0.x + a1.x) + (a2.x + a3.x), (a0.y + a1.y) + (a2.y + a3.y),
-                      (a0.z + a1.z) + (a2.z + a3.z), (a0.w + a1.w) + (a2.w + a3.w));
-      lds_barrier();
-      const float4* fin = reinterpret_cast<const float4*>(sfin + hg * 1024);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4 v = fin[r * 64 + lane];
-        st[4 * r] = v.x;
-        st[4 * r + 1] = v.y;
-        st[4 * r + 2] = v.z;
-        st[4 * r + 3] = v.w;
-      }
-    }
-    // ---- logits: lane holds head hl, keys 8(i/4) + 4hh + i%4
+    // ---- logits of chunk c: lane holds head hl, MFMA rows 8(i/4) + 4hh + i%4;
+    // bit m of vmask = key key_of_row(m) is real
+    const int kr = key_of_row(hl);
+    const int slot = min(max(c * kKC + kr - sl_lo, 0), kMaxSel - 1);  // used for a selection chunk
+    const bool sel_ok = s_ent[slot] >= 0, win_ok = (c - nm) * kKC + kr < n_swa;
+    const uint32_t vmask = (uint32_t)__ballot(main_chunk ? sel_ok : win_ok);
     const float ks = main_chunk ? 1.0f : swa_scale;
     const float fs = ks * sm_log2;
     float lg[16];
@@ -325,43 +333,27 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
       const int key = 8 * (i / 4) + 4 * hh + (i % 4);
       lg[i] = ((vmask >> key) & 1u) ? st[i] * fs : -INFINITY;
     }
-    // Lazy reference maximum: the two lanes of a head only need to agree on it
-    // when one of them sees a logit more than 2^kLazy above it.
+    // Lazy reference maximum: it only moves (for both lanes of a head) when a
+    // logit exceeds it by more than 2^kLazy; everything but the rare rescale of
+    // O is branch-free, so this chunk's softmax and the next chunk's S^T MFMAs
+    // form one block the scheduler can interleave.
     float lmax = lg[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, lg[i]);
-    const bool grow = lmax > m_ref + kLazy || (m_ref == -INFINITY && lmax != -INFINITY);
+    const float cmax = fmaxf(lmax, __shfl_xor(lmax, 32));
+    const bool up = cmax > m_ref + kLazy || (m_ref == -INFINITY && cmax != -INFINITY);
+    const float alpha = up ? (m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - cmax)) : 1.0f;
+    m_ref = up ? cmax : m_ref;
+    l_run *= alpha;
     // P (times the key scale) in fp16: A operand of k-step t = elements 8t .. 8t+7
-    auto probs = [&](f16x8_t (&pa)[2]) {
+    f16x8_t pa[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i] - m_ref);
-        l_run += p;
-        pa[i / 8][i % 8] = (_Float16)(p * ks);
-      }
-    };
-    // O += P·V: V slots follow P's key order (16t + 8(s/4) + 4hh + s%4); key vk + 8
-    // starts 8 rows and 32 bytes after key vk, key 16 + vk 16 rows after.
-    auto pv = [&](const f16x8_t (&pa)[2]) {
-      const uint8_t* vb = kb + pv_off;
-#pragma unroll
-      for (int n = 0; n < DH / 32; ++n) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const f16x4_t lo = lds_read_tr(vb + 16 * t * KSTB + 64 * n);
-          const f16x4_t hi = lds_read_tr(vb + (16 * t + 8) * KSTB + 32 + 64 * n);
-          o[n] = mfma32x32x16_f16(pa[t], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), o[n]);
-        }
-      }
-    };
-    if (__ballot(grow)) {
-      const float cmax = fmaxf(lmax, __shfl_xor(lmax, 32));
-      float alpha = 1.0f;
-      if (cmax > m_ref + kLazy || (m_ref == -INFINITY && cmax != -INFINITY)) {
-        alpha = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - cmax);
-        m_ref = cmax;
-      }
-      l_run *= alpha;
+    for (int i = 0; i < 16; ++i) {
+      const float p = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i] - m_ref);
+      l_run += p;
+      pa[i / 8][i % 8] = (_Float16)(p * ks);
+    }
+    if (__ballot(up)) {
       float al[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) al[i] = __shfl(alpha, 8 * (i / 4) + 4 * hh + (i % 4));
@@ -371,9 +363,27 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
         for (int i = 0; i < 16; ++i) o[n][i] *= al[i];
       }
     }
-    f16x8_t pa[2];
-    probs(pa);
-    pv(pa);
+    // ---- O += P·V: V slot s of k-step t = MFMA row 16t + 8(s/4) + 4hh + s%4, i.e.
+    // key 16t + 4(s%4) + hh (+2 for s >= 4)
+    {
+      const uint8_t* vb = kv[buf] + pv_off;
+#pragma unroll
+      for (int n = 0; n < DH / 32; ++n) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f16x4_t lo = lds_read_tr(vb + 16 * t * KSTB + 64 * n);
+          const f16x4_t hi = lds_read_tr(vb + (16 * t + 2) * KSTB + 64 * n);
+          o[n] = mfma32x32x16_f16(pa[t], __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), o[n]);
+        }
+      }
+    }
+    // ---- decode chunk c+2 into the buffer chunk c-1 used, load chunk c+3
+    if (c + 2 < c_end) {
+      decode(kv[buf == 0 ? 2 : buf - 1], c + 2 < nm);
+      if (c + 3 < c_end) load_raw(c + 3);
+    }
+    // ---- logits of chunk c+1
+    if (c + 1 < c_end) st = exchange(stn);
   }
 
   // ---- epilogue: O element i of lane l is head 8(i/4) + 4hh + i%4, dim l%32
