@@ -151,7 +151,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   constexpr int NCL = VPT >= 32 ? VPT / 32 : 1;  // code loads
   constexpr int NLD = NCL + 1 > VPT / 16 ? NCL + 1 : VPT / 16;
   u32x4_t raw[NLD];
-  auto load_raw = [&](int c) {
+  auto load_raw = [&](u32x4_t (&raw)[NLD], int c) {
     const bool mc = c < nm;
     const int e = mc ? max(s_ent[c * kKC + dkey - sl_lo], 0) : 0;  // padding reads entry 0, masked later
     const size_t ent = (size_t)b * N + e;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     }
   };
   // ---- decode the raw registers into one LDS buffer (exact fp16)
-  auto decode = [&](uint8_t* buf, bool main_chunk) {
+  auto decode = [&](const u32x4_t (&raw)[NLD], uint8_t* buf, bool main_chunk) {
     uint8_t* rp = buf + dkey * KSTB + dseg * NU * 16;
     if (main_chunk) {
       // this thread's scale bytes: offset (dseg*NSB) mod 16 of slot NCL
@@ -211,8 +211,10 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     }
   };
 
-  // the first chunk's bytes are requested before the query, so the two waits overlap
-  if (c_begin < c_end) load_raw(c_begin);
+  // the first two chunks' bytes are requested before the query, so the waits overlap
+  u32x4_t raw2[NLD];
+  if (c_begin < c_end) load_raw(raw, c_begin);
+  if (c_begin + 1 < c_end) load_raw(raw2, c_begin + 1);
 
   // ---- this wave's query quarter (B operand of S^T), scaled into fp16 exactly
   f16x8_t qh[DH / 16];
@@ -302,11 +304,10 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   // the logits of c_begin summed
   f32x16_t st = f32x16_t{};
   if (c_begin < c_end) {
-    decode(kv[0], c_begin < nm);
+    decode(raw, kv[0], c_begin < nm);
     if (c_begin + 1 < c_end) {
-      load_raw(c_begin + 1);
-      decode(kv[1], c_begin + 1 < nm);
-      if (c_begin + 2 < c_end) load_raw(c_begin + 2);
+      decode(raw2, kv[1], c_begin + 1 < nm);
+      if (c_begin + 2 < c_end) load_raw(raw, c_begin + 2);
     }
     lds_barrier();
     st = exchange(qk(kv[0]));
@@ -379,8 +380,8 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     }
     // ---- decode chunk c+2 into the buffer chunk c-1 used, load chunk c+3
     if (c + 2 < c_end) {
-      decode(kv[buf == 0 ? 2 : buf - 1], c + 2 < nm);
-      if (c + 3 < c_end) load_raw(c + 3);
+      decode(raw, kv[buf == 0 ? 2 : buf - 1], c + 2 < nm);
+      if (c + 3 < c_end) load_raw(raw, c + 3);
     }
     // ---- logits of chunk c+1
     if (c + 1 < c_end) st = exchange(stn);
