@@ -402,7 +402,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
 __global__ __launch_bounds__(kSelThreads) void topk_row_kernel(
     const float* __restrict__ scores, int N, const int* __restrict__ valid_len,
     const int* __restrict__ cand_map, int K, int* __restrict__ out) {
-  __shared__ float s_row[kRowCap];                // 64 KB
   __shared__ unsigned long long keys[kTopkCap];   // 64 KB
   __shared__ __attribute__((aligned(16))) int chosen[2048];
   __shared__ uint32_t hist[256];
@@ -433,42 +432,48 @@ __global__ __launch_bounds__(kSelThreads) void topk_row_kernel(
     }
     total = n;
   } else {
+    // The row stays in registers (thread t holds entries t + 1024u).  Chunks are
+    // sets of a thread's entries: any C >= K disjoint non-empty chunks have C
+    // distinct maxima, so the K-th best score is at least the smallest of them.
+    // C = 512 chunks (threads t and t + 512 together) when K <= 512, else one
+    // chunk per thread (C = 1024) or per half of a thread's entries (C = 2048).
+    float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = tid + u * kSelThreads;
-      if (i < n) s_row[i] = rv[u];
+      const float v = i < n ? rv[u] : -INFINITY;
+      if (u < kPer / 2) m0 = fmaxf(m0, v);
+      else m1 = fmaxf(m1, v);
+    }
+    float cm;  // this thread's share of min over chunk maxima
+    if (K <= kSelThreads / 2) {
+      float* pm = reinterpret_cast<float*>(keys);  // keys are written only later
+      pm[tid] = fmaxf(m0, m1);
+      __syncthreads();
+      cm = tid < kSelThreads / 2 ? fmaxf(pm[tid], pm[tid + kSelThreads / 2]) : INFINITY;
+    } else if (K <= kSelThreads) {
+      cm = fmaxf(m0, m1);
+    } else {
+      cm = fminf(m0, m1);  // an empty half (max -inf) sends the row to the exact path below
     }
     if (tid == 0) misc[0] = 0;
-    __syncthreads();
-    // C >= K chunks of clen entries: their maxima are C distinct entries, so the
-    // K-th best score is at least the smallest of them
-    const int clen = n / K;
-    const int C = (n + clen - 1) / clen;
-    float mn = INFINITY;
-    for (int c = tid; c < C; c += kSelThreads) {
-      const int lo = c * clen, hi = min(lo + clen, n);
-      float mx = -INFINITY;
-#pragma unroll 8
-      for (int i = lo; i < hi; ++i) mx = fmaxf(mx, s_row[i]);
-      mn = fminf(mn, mx);
-    }
-    mn = wave_min(mn);
-    if (lane == 0) red[wave] = mn;
+    cm = wave_min(cm);
+    if (lane == 0) red[wave] = cm;
     __syncthreads();
     float T = red[0];
 #pragma unroll
     for (int w2 = 1; w2 < kSelThreads / 64; ++w2) T = fminf(T, red[w2]);
     const uint32_t tk = mono_key(T);
-    for (int base = 0; base < n; base += kSelThreads) {
-      const int i = base + tid;
-      const float sv = i < n ? s_row[i] : 0.0f;
-      const bool take = i < n && mono_key(sv) >= tk;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kSelThreads;
+      const bool take = i < n && mono_key(rv[u]) >= tk;
       const unsigned long long m = __ballot(take);
       int wpos = 0;
       if (lane == 0 && m) wpos = atomicAdd(&misc[0], __popcll(m));
       wpos = __shfl(wpos, 0);
       const int pos = wpos + __popcll(m & ((1ull << lane) - 1ull));
-      if (take && pos < kTopkCap) keys[pos] = make_key(sv, i);
+      if (take && pos < kTopkCap) keys[pos] = make_key(rv[u], i);
     }
     __syncthreads();
     total = misc[0];

@@ -95,7 +95,8 @@ def test_prefill_scores(B, Tq, N, h_i, d_i, m, pos):
                                         (4, 8192, 2048, "ties"), (2, 20000, 1, "gauss"),
                                         (3, 100, 512, "gauss"), (2, 300000, 2048, "gauss"),
                                         (64, 12288, 512, "gauss"), (5, 16384, 2048, "gauss"),
-                                        (3, 16384, 512, "ties"), (4, 9000, 1, "gauss")])
+                                        (3, 16384, 512, "ties"), (4, 9000, 1, "gauss"),
+                                        (2, 10000, 700, "gauss"), (2, 9000, 1500, "gauss")])
 def test_topk_paths(R, N, K, kind):
     rng = np.random.default_rng(N + K)
     if kind == "ties":
