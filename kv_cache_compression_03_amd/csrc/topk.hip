@@ -72,9 +72,14 @@ CSA2_DEV int key_index(unsigned long long k) { return (int)(0xFFFFFFFFu - (uint3
 
 // ---------------------------------------------------------------- wide passes
 
+constexpr int kChunksPerWave = 4;
+
+// Short chunks (<= 128 entries): one wave per kChunksPerWave consecutive chunks,
+// every load requested together.  Long chunks: one wave per chunk, 8 loads per
+// lane in flight.
 __global__ __launch_bounds__(256) void topk_chunkmax_kernel(const float* __restrict__ scores, int N,
                                                             const int* __restrict__ valid_len, int K,
-                                                            float* __restrict__ cmax,
+                                                            int cpw, float* __restrict__ cmax,
                                                             int* __restrict__ cnt) {
   const int r = blockIdx.y;
   const int n = row_len(valid_len, r, N);
@@ -82,19 +87,40 @@ __global__ __launch_bounds__(256) void topk_chunkmax_kernel(const float* __restr
   if (blockIdx.x == 0 && threadIdx.x == 0) cnt[r] = 0;
   const int clen = n / K;  // >= 4 because n > kTopkCap >= 4K
   const int C = (n + clen - 1) / clen;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= C) return;
+  const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * cpw;
+  if (c0 >= C) return;
   const int lane = threadIdx.x & 63;
   const float* row = scores + (size_t)r * N;
-  const int lo = c * clen, hi = min(lo + clen, n);
-  float mx = -INFINITY;
-  for (int i = lo + lane; i < hi; i += 64) mx = fmaxf(mx, row[i]);
-  mx = wave_max(mx);
-  if (lane == 0) cmax[(size_t)r * 2 * K + c] = mx;
+  if (cpw == 1) {
+    const int lo = c0 * clen, hi = min(lo + clen, n);
+    float mx = -INFINITY;
+#pragma unroll 8
+    for (int i = lo + lane; i < hi; i += 64) mx = fmaxf(mx, row[i]);
+    mx = wave_max(mx);
+    if (lane == 0) cmax[(size_t)r * 2 * K + c0] = mx;
+    return;
+  }
+  float v[kChunksPerWave][2];
+#pragma unroll
+  for (int j = 0; j < kChunksPerWave; ++j) {
+    const int lo = (c0 + j) * clen, hi = min(lo + clen, n);
+    v[j][0] = c0 + j < C && lo + lane < hi ? row[lo + lane] : -INFINITY;
+    v[j][1] = c0 + j < C && lo + 64 + lane < hi ? row[lo + 64 + lane] : -INFINITY;
+  }
+#pragma unroll
+  for (int j = 0; j < kChunksPerWave; ++j) {
+    if (c0 + j >= C) break;
+    const int lo = (c0 + j) * clen, hi = min(lo + clen, n);
+    float mx = fmaxf(v[j][0], v[j][1]);
+    for (int i = lo + 128 + lane; i < hi; i += 64) mx = fmaxf(mx, row[i]);
+    mx = wave_max(mx);
+    if (lane == 0) cmax[(size_t)r * 2 * K + c0 + j] = mx;
+  }
 }
 
-constexpr int kFilterPerThread = 16;
-
+// Entries per filter thread: more for long rows, so fewer workgroups contend for
+// a row's candidate counter.
+template <int PER>
 __global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restrict__ scores, int N,
                                                           const int* __restrict__ valid_len, int K,
                                                           const float* __restrict__ cmax,
@@ -104,7 +130,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restric
   const int r = blockIdx.y;
   const int n = row_len(valid_len, r, N);
   if (n <= kTopkCap) return;
-  const long long e0 = (long long)blockIdx.x * 256 * kFilterPerThread;
+  const long long e0 = (long long)blockIdx.x * 256 * PER;
   if (e0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int clen = n / K;
@@ -112,7 +138,14 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restric
   __shared__ float red[4];
   __shared__ int wsum[4];
   __shared__ int base;
-  // C <= 2K <= 4096 chunk maxima: every load of a thread issued at once
+  // this thread's scores and (C <= 2K <= 4096) chunk maxima, all requested at once
+  const float* row = scores + (size_t)r * N;
+  float sv[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const long long e = e0 + it * 256 + tid;
+    sv[it] = e < n ? row[e] : 0.0f;
+  }
   float mn = INFINITY;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -123,17 +156,14 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restric
   if (lane == 0) red[wave] = mn;
   __syncthreads();
   const uint32_t tk = mono_key(fminf(fminf(red[0], red[1]), fminf(red[2], red[3])));
-  const float* row = scores + (size_t)r * N;
-  float sv[kFilterPerThread];
-  uint32_t take = 0;
+  uint64_t take = 0;
 #pragma unroll
-  for (int it = 0; it < kFilterPerThread; ++it) {
+  for (int it = 0; it < PER; ++it) {
     const long long e = e0 + it * 256 + tid;
-    sv[it] = e < n ? row[e] : 0.0f;
-    take |= (e < n && mono_key(sv[it]) >= tk) ? (1u << it) : 0u;
+    take |= (e < n && mono_key(sv[it]) >= tk) ? (1ull << it) : 0ull;
   }
   // workgroup prefix of the per-thread candidate counts, then one atomic per workgroup
-  const int mine = __popc(take);
+  const int mine = __popcll(take);
   int x = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -147,8 +177,8 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const float* __restric
   int pos = base + x - mine;
   for (int w2 = 0; w2 < wave; ++w2) pos += wsum[w2];
 #pragma unroll
-  for (int it = 0; it < kFilterPerThread; ++it) {
-    if (take & (1u << it)) {
+  for (int it = 0; it < PER; ++it) {
+    if (take & (1ull << it)) {
       if (pos < kTopkCap) {
         cscore[(size_t)r * kTopkCap + pos] = sv[it];
         cidx[(size_t)r * kTopkCap + pos] = (int)(e0 + it * 256 + tid);
@@ -531,11 +561,18 @@ hipError_t launch_topk(const float* scores, int R, int N, const int* valid_len, 
     return hipGetLastError();
   }
   {
-    hipLaunchKernelGGL(topk_chunkmax_kernel, dim3((2 * K + 3) / 4, R), dim3(256), 0, st, scores, N,
-                       valid_len, K, ws.cmax, ws.cnt);
-    const int fx = (N + 256 * kFilterPerThread - 1) / (256 * kFilterPerThread);
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(fx, R), dim3(256), 0, st, scores, N, valid_len, K,
-                       ws.cmax, ws.cnt, ws.cscore, ws.cidx);
+    const int cpw = N / K <= 128 ? kChunksPerWave : 1;  // chunk length <= N / K
+    hipLaunchKernelGGL(topk_chunkmax_kernel, dim3((2 * K + 4 * cpw - 1) / (4 * cpw), R), dim3(256), 0,
+                       st, scores, N, valid_len, K, cpw, ws.cmax, ws.cnt);
+    if (N >= (1 << 18)) {
+      const int fx = (N + 256 * 64 - 1) / (256 * 64);
+      hipLaunchKernelGGL(topk_filter_kernel<64>, dim3(fx, R), dim3(256), 0, st, scores, N, valid_len, K,
+                         ws.cmax, ws.cnt, ws.cscore, ws.cidx);
+    } else {
+      const int fx = (N + 256 * 16 - 1) / (256 * 16);
+      hipLaunchKernelGGL(topk_filter_kernel<16>, dim3(fx, R), dim3(256), 0, st, scores, N, valid_len, K,
+                         ws.cmax, ws.cnt, ws.cscore, ws.cidx);
+    }
   }
   hipLaunchKernelGGL(topk_select_kernel, dim3(R), dim3(kSelThreads),
                      kTopkCap * sizeof(unsigned long long), st, scores, N, valid_len, cand_map, K,
