@@ -600,6 +600,10 @@ CSA2_DEV int visible(const int* q_pos, int m, int r, int N) {
   return (int)(v < 0 ? 0 : (v > N ? N : v));
 }
 
+constexpr int kBlocksPerWave = 4;
+
+// Block maxima: one wave per kBlocksPerWave consecutive blocks, the first 128
+// entries of each block requested together (blocks are G <= 256 entries).
 __global__ __launch_bounds__(256) void pool_blockmax_kernel(const float* __restrict__ scores, int N,
                                                             const int* __restrict__ q_pos, int m,
                                                             int G, int nblk_max,
@@ -607,21 +611,46 @@ __global__ __launch_bounds__(256) void pool_blockmax_kernel(const float* __restr
                                                             int* __restrict__ nblk_out) {
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nblk_max) return;
+  const int b0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kBlocksPerWave;
+  if (b0 >= nblk_max) return;
   const int n = visible(q_pos, m, r, N);
   const int nblk = (n + G - 1) / G;
-  if (blk == 0 && lane == 0) nblk_out[r] = nblk;
-  float mx = -INFINITY;
-  if (blk < nblk) {
-    const float* row = scores + (size_t)r * N;
-    const int lo = blk * G, hi = min(lo + G, n);
-    for (int i = lo + lane; i < hi; i += 64) mx = fmaxf(mx, row[i]);
-    mx = wave_max(mx);
+  if (b0 == 0 && lane == 0) nblk_out[r] = nblk;
+  const float* row = scores + (size_t)r * N;
+  float v[kBlocksPerWave][2];
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j) {
+    const int lo = (b0 + j) * G, hi = min(lo + G, n);
+    const bool live = b0 + j < nblk;
+    v[j][0] = live && lo + lane < hi ? row[lo + lane] : -INFINITY;
+    v[j][1] = live && lo + 64 + lane < hi ? row[lo + 64 + lane] : -INFINITY;
   }
-  if (lane == 0) bmax[(size_t)r * nblk_max + blk] = mx;
+#pragma unroll
+  for (int j = 0; j < kBlocksPerWave; ++j) {
+    const int blk = b0 + j;
+    if (blk >= nblk_max) break;
+    float mx = -INFINITY;
+    if (blk < nblk) {
+      const int lo = blk * G, hi = min(lo + G, n);
+      mx = fmaxf(v[j][0], v[j][1]);
+      for (int i = lo + 128 + lane; i < hi; i += 64) mx = fmaxf(mx, row[i]);
+      mx = wave_max(mx);
+    }
+    if (lane == 0) bmax[(size_t)r * nblk_max + blk] = mx;
+  }
 }
 
+CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Per selected block, its PE best entries (score, then lower index) in ascending
+// index order.  One wave per block, KPL = ceil(G/64) keys per lane; each pick is
+// an arg-max over the wave: the 32-bit score key is reduced first, and the full
+// (score, index) key only when several lanes tie on the score.
+template <int KPL>
 __global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restrict__ scores, int N,
                                                           const int* __restrict__ q_pos, int m, int G,
                                                           int PB, int PE,
@@ -645,9 +674,9 @@ __global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restric
   const int lo = blk * G;
   const int len = min(G, n - lo);
   const float* row = scores + (size_t)r * N;
-  unsigned long long key[4];
+  unsigned long long key[KPL];  // 0 = no entry (a real key is never 0)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < KPL; ++q) {
     const int j = lane + 64 * q;
     key[q] = j < len ? make_key(row[lo + j], lo + j) : 0ull;
   }
@@ -658,12 +687,22 @@ __global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restric
     if (p < cntb) {
       unsigned long long best = key[0];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
-      best = wave_max_u64(best);
-      if (lane == p) mine = key_index(best);
+      for (int q = 1; q < KPL; ++q) best = key[q] > best ? key[q] : best;
+      const uint32_t hi = (uint32_t)(best >> 32);
+      const uint32_t hmax = wave_max_u32(hi);
+      const unsigned long long tied = __ballot(hi == hmax);
+      unsigned long long win;
+      if (__popcll(tied) == 1) {
+        const int wl = __ffsll((long long)tied) - 1;
+        win = ((unsigned long long)hmax << 32) |
+              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, wl);
+      } else {
+        win = wave_max_u64(hi == hmax ? best : 0ull);
+      }
+      if (lane == p) mine = key_index(win);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (key[q] == best) key[q] = 0ull;
+      for (int q = 0; q < KPL; ++q)
+        if (key[q] == win) key[q] = 0ull;
     }
   }
   // ascending order of the picks: rank = number of smaller picks
@@ -690,12 +729,21 @@ hipError_t launch_pool(const float* scores, int R, int N, const int* q_pos, int 
   int* selblk = reinterpret_cast<int*>(p);
   p += align256((size_t)R * PB * sizeof(int));
   TopkWs tws = topk_ws_carve(p, R, PB);
-  hipLaunchKernelGGL(pool_blockmax_kernel, dim3((nb + 3) / 4, R), dim3(256), 0, st, scores, N, q_pos,
+  hipLaunchKernelGGL(pool_blockmax_kernel, dim3((nb + 4 * kBlocksPerWave - 1) / (4 * kBlocksPerWave), R),
+                     dim3(256), 0, st, scores, N, q_pos,
                      m, G, nb, bmax, nblk);
   hipError_t e = launch_topk(bmax, R, nb, nblk, nullptr, PB, selblk, tws, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pool_gather_kernel, dim3((PB + 3) / 4, R), dim3(256), 0, st, scores, N, q_pos, m,
-                     G, PB, PE, selblk, pool, pool_len);
+  const dim3 ggrid((PB + 3) / 4, R);
+  if (G <= 64)
+    hipLaunchKernelGGL(pool_gather_kernel<1>, ggrid, dim3(256), 0, st, scores, N, q_pos, m, G, PB, PE,
+                       selblk, pool, pool_len);
+  else if (G <= 128)
+    hipLaunchKernelGGL(pool_gather_kernel<2>, ggrid, dim3(256), 0, st, scores, N, q_pos, m, G, PB, PE,
+                       selblk, pool, pool_len);
+  else
+    hipLaunchKernelGGL(pool_gather_kernel<4>, ggrid, dim3(256), 0, st, scores, N, q_pos, m, G, PB, PE,
+                       selblk, pool, pool_len);
   return hipGetLastError();
 }
 
