@@ -96,7 +96,8 @@ def test_prefill_scores(B, Tq, N, h_i, d_i, m, pos):
                                         (3, 100, 512, "gauss"), (2, 300000, 2048, "gauss"),
                                         (64, 12288, 512, "gauss"), (5, 16384, 2048, "gauss"),
                                         (3, 16384, 512, "ties"), (4, 9000, 1, "gauss"),
-                                        (2, 10000, 700, "gauss"), (2, 9000, 1500, "gauss")])
+                                        (2, 10000, 700, "gauss"), (2, 9000, 1500, "gauss"),
+                                        (4, 40000, 512, "short")])
 def test_topk_paths(R, N, K, kind):
     rng = np.random.default_rng(N + K)
     if kind == "ties":
@@ -105,6 +106,8 @@ def test_topk_paths(R, N, K, kind):
         s = rng.standard_normal((R, N)).astype(np.float32)
     vl = rng.integers(N // 2, N + 1, R).astype(np.int32)
     vl[0] = N
+    if kind == "short":   # rows whose visible prefix fits the direct path, and one shorter than K
+        vl[1:] = [8192, 3000, 300]
     out = bd().csa2_topk(dev(s), K, valid_len=dev(vl))
     torch.cuda.synchronize()
     out = out.cpu().numpy()
