@@ -176,7 +176,7 @@ CSA2_API int csa2_index_reindex(const void* q_idx, const float* w, const void* k
  * Limits: d in {256, 512}, H_q % 16 == 0, K <= 2048.
  * Precision: products are exact (entries, window values and probabilities are
  * carried in fp16 or bf16, both exact for the decoded values) and accumulate in
- * fp32.  When H_q % 32 == 0, |swa_scale| <= 128 and codes, scales and swa are
+ * fp32.  When H_q % 32 == 0, 0 < swa_scale <= 128 and codes, scales and swa are
  * 16-byte aligned, the fp16 kernel runs (probabilities with 11 significant bits,
  * queries scaled into fp16 by a power of two per head); otherwise the bf16
  * kernel (probabilities as a bf16 pair, 16 bits).

@@ -36,8 +36,9 @@ static inline int xcd_grid(int rows, int per_row) {
 }
 
 // fp16 kernel (attn_f16.hip): 32-head groups, whole selection of a split staged.
-// Usable when H_q is a multiple of 32, d is 256 or 512 and |swa_scale| <= 128 (so
-// that probabilities times the window scale stay inside fp16 range).
+// Usable when H_q is a multiple of 32, d is 256 or 512 and 0 < swa_scale <= 128
+// (probabilities times the window scale stay inside fp16 range and are formed as
+// one power of two).
 bool attn_f16_supported(int H_q, int d, float swa_scale);
 hipError_t launch_sparse_attn_f16(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                                   int N, const int* sel, int K, const uint8_t* swa, float swa_scale,

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   constexpr int VPT = kKC * D / NT;  // values each thread decodes per chunk
   constexpr int NU = VPT / 8;        // 16-byte LDS units each thread writes per chunk
   constexpr int NSB = VPT / 16;      // E4M3 block scales per thread
-  static_assert(VPT >= 16 && VPT % 16 == 0 && DH % 32 == 0, "decode split");
+  static_assert(VPT >= 16 && VPT % 16 == 0 && NSB <= 4 && DH % 32 == 0, "decode split");
   // Key row k starts at k*KSTB bytes, i.e. in 16-byte bank slot k mod 16.  The
   // decode writes and the S^T operand reads touch one column of 16 keys per
   // instruction (16 distinct slots); with the row order of key_of_row() each
@@ -104,6 +104,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   __shared__ __attribute__((aligned(16))) float sx[NW * 4 * 64 * 4];     // partial logit tiles
   __shared__ __attribute__((aligned(16))) float sfin[HG2 * 4 * 64 * 4];  // summed tiles
   __shared__ int s_ent[kMaxSel];  // entry of each selection slot this split reads
+  __shared__ float s_qmax[NW][32];  // per wave, largest |q| of each of its heads over its dims
 
   int row, split;
   if (!xcd_map(blockIdx.x, rows, n_splits * head_groups, row, split)) return;
@@ -175,17 +176,19 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
       const u32x4_t sv = raw[NCL];
       const uint32_t sw = ((so >> 2) == 0 ? sv[0] : (so >> 2) == 1 ? sv[1] : (so >> 2) == 2 ? sv[2] : sv[3]) >>
                           (8 * (so & 3));
-      // each E4M3 block scale = 2^E (applied by the conversion) x M, M in [1, 2)
-      float p2[NSB];
+      // the E4M3 block scales as exact fp16 values (two per conversion); an E2M1
+      // value times its scale has at most 6 significant bits, so the fp16 product
+      // below is exact
       f16x2_t mm[NSB];
-#pragma unroll
-      for (int j = 0; j < NSB; ++j) {
-        const float sc = e4m3_decode((sw >> (8 * j)) & 0xFFu);
-        const uint32_t bits = __float_as_uint(sc);
-        const bool z = sc == 0.0f;
-        p2[j] = z ? 1.0f : __uint_as_float(bits & 0x7F800000u);
-        const _Float16 m = z ? (_Float16)0.0f : (_Float16)__uint_as_float((bits & 0x807FFFFFu) | 0x3F800000u);
-        mm[j] = f16x2_t{m, m};
+      {
+        const f16x2_t s01 = __builtin_bit_cast(f16x2_t, fp8x2_f16<false>(sw));
+        mm[0] = f16x2_t{s01[0], s01[0]};
+        if constexpr (NSB >= 2) mm[1] = f16x2_t{s01[1], s01[1]};
+        if constexpr (NSB >= 4) {
+          const f16x2_t s23 = __builtin_bit_cast(f16x2_t, fp8x2_f16<true>(sw));
+          mm[2] = f16x2_t{s23[0], s23[0]};
+          mm[3] = f16x2_t{s23[1], s23[1]};
+        }
       }
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -194,10 +197,10 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
         if constexpr (VPT >= 32) w = raw[u / 4][u % 4];
         else w = (dseg & 1) ? raw[0][2 + u] : raw[0][u];
         const int j = u / 2;
-        const u32x4_t pk = {__builtin_bit_cast(uint32_t, fp4x2_f16<0>(w, p2[j]) * mm[j]),
-                            __builtin_bit_cast(uint32_t, fp4x2_f16<1>(w, p2[j]) * mm[j]),
-                            __builtin_bit_cast(uint32_t, fp4x2_f16<2>(w, p2[j]) * mm[j]),
-                            __builtin_bit_cast(uint32_t, fp4x2_f16<3>(w, p2[j]) * mm[j])};
+        const u32x4_t pk = {__builtin_bit_cast(uint32_t, fp4x2_f16<0>(w, 1.0f) * mm[j]),
+                            __builtin_bit_cast(uint32_t, fp4x2_f16<1>(w, 1.0f) * mm[j]),
+                            __builtin_bit_cast(uint32_t, fp4x2_f16<2>(w, 1.0f) * mm[j]),
+                            __builtin_bit_cast(uint32_t, fp4x2_f16<3>(w, 1.0f) * mm[j])};
         *reinterpret_cast<u32x4_t*>(rp + 16 * u) = pk;
       }
     } else {
@@ -216,12 +219,15 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   if (c_begin < c_end) load_raw(raw, c_begin);
   if (c_begin + 1 < c_end) load_raw(raw2, c_begin + 1);
 
-  // ---- this wave's query quarter (B operand of S^T), scaled into fp16 exactly
+  // ---- this wave's query quarter (B operand of S^T), moved into fp16 exactly by
+  // a power of two per head that the four dim-quarter waves share (so partial
+  // logit tiles add without rescaling); the exponent needs every quarter's
+  // largest |q|, which is exchanged at the prologue's barrier
   f16x8_t qh[DH / 16];
-  float qs;  // logits of this wave's quarter = S * qs
+  float qs;  // logits of head hl = (sum of the partial tiles) * qs
+  u32x4_t qraw[DH / 16];
   {
     const uint16_t* qr = q + ((size_t)row * H_q + head0 + hl) * D + dim0 + 8 * hh;
-    u32x4_t qraw[DH / 16];
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) qraw[s] = *reinterpret_cast<const u32x4_t*>(qr + 16 * s);
     float mx = 0.0f;
@@ -234,6 +240,13 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (hh == 0) s_qmax[wave][hl] = mx;
+  }
+  auto convert_q = [&]() {
+    const int hg = wave % HG2;
+    float mx = s_qmax[hg][hl];
+#pragma unroll
+    for (int k = 1; k < DS; ++k) mx = fmaxf(mx, s_qmax[hg + HG2 * k][hl]);
     int e = 0;  // the head's largest |q| x 2^-e lands in [2^14, 2^15)
     if (mx > 0.0f) e = min(126, max(-126, (int)((__float_as_uint(mx) >> 23) & 255u) - 127 - 14));
     const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
@@ -246,12 +259,13 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
         qh[s][2 * k + 1] = (_Float16)(__uint_as_float(qraw[s][k] & 0xFFFF0000u) * inv);
       }
     }
-  }
+  };
 
   f32x16_t o[DH / 32];
 #pragma unroll
   for (int n = 0; n < DH / 32; ++n) o[n] = f32x16_t{};
   float m_ref = -INFINITY, l_run = 0.0f;
+  const float log2_swa = log2f(swa_scale), inv_swa = 1.0f / swa_scale;  // swa_scale > 0 here
 
   // S^T operand: MFMA row hl = key key_of_row(hl), dims dim0 + 16s + 8hh
   // (+32 bytes per step s)
@@ -278,8 +292,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     float4* mine = reinterpret_cast<float4*>(sx + wave * 1024);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      mine[r * 64 + lane] = make_float4(st[4 * r] * qs, st[4 * r + 1] * qs, st[4 * r + 2] * qs,
-                                        st[4 * r + 3] * qs);
+      mine[r * 64 + lane] = make_float4(st[4 * r], st[4 * r + 1], st[4 * r + 2], st[4 * r + 3]);
     lds_barrier();
     const int hg = wave % HG2;
     const float4* grp = reinterpret_cast<const float4*>(sx + hg * 1024) + dq * 64 + lane;
@@ -310,6 +323,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
       if (c_begin + 2 < c_end) load_raw(raw, c_begin + 2);
     }
     lds_barrier();
+    convert_q();
     st = exchange(qk(kv[0]));
   }
   for (int c = c_begin; c < c_end; ++c) {
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     const bool sel_ok = s_ent[slot] >= 0, win_ok = (c - nm) * kKC + kr < n_swa;
     const uint32_t vmask = (uint32_t)__ballot(main_chunk ? sel_ok : win_ok);
     const float ks = main_chunk ? 1.0f : swa_scale;
-    const float fs = ks * sm_log2;
+    const float fs = ks * sm_log2 * qs;
     float lg[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -346,14 +360,19 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     const float alpha = up ? (m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - cmax)) : 1.0f;
     m_ref = up ? cmax : m_ref;
     l_run *= alpha;
-    // P (times the key scale) in fp16: A operand of k-step t = elements 8t .. 8t+7
+    // P times the key scale, in fp16 (A operand of k-step t = elements 8t .. 8t+7):
+    // p * ks = exp2(lg - (m_ref - log2 ks)), and the row sum gains sum(p * ks) / ks.
+    // While no key has been seen (m_ref = -inf) every lg is -inf and p = 0.
+    const float mp = m_ref == -INFINITY ? 0.0f : m_ref - (main_chunk ? 0.0f : log2_swa);
+    float psum = 0.0f;
     f16x8_t pa[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lg[i] - m_ref);
-      l_run += p;
-      pa[i / 8][i % 8] = (_Float16)(p * ks);
+      const float pk = __builtin_amdgcn_exp2f(lg[i] - mp);
+      psum += pk;
+      pa[i / 8][i % 8] = (_Float16)pk;
     }
+    l_run += main_chunk ? psum : psum * inv_swa;
     if (__ballot(up)) {
       float al[16];
 #pragma unroll
@@ -422,7 +441,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
 }
 
 bool attn_f16_supported(int H_q, int d, float swa_scale) {
-  return H_q % 32 == 0 && (d == 256 || d == 512) && fabsf(swa_scale) <= 128.0f;
+  return H_q % 32 == 0 && (d == 256 || d == 512) && swa_scale > 0.0f && swa_scale <= 128.0f;
 }
 
 hipError_t launch_sparse_attn_f16(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,

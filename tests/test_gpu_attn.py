@@ -98,7 +98,7 @@ def test_query_magnitudes(q_exp):
         compare_lse(lse[b, 0], q[b, 0], codes[b], scales[b], sel[b, 0], swa[b])
 
 
-@pytest.mark.parametrize("swa_scale", [0.37, 100.0, 200.0])   # 200: above the fp16 kernel's limit
+@pytest.mark.parametrize("swa_scale", [0.37, 100.0, 200.0, -0.5])   # 200, -0.5: bf16 kernel
 def test_swa_scale_and_prefill_positions(swa_scale):
     rng = np.random.default_rng(11)
     B, Tq, H, d, N, K, S, n_win = 1, 7, 32, 512, 4000, 64, 300, 128
