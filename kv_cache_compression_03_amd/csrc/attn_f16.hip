@@ -343,10 +343,22 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     const float ks = main_chunk ? 1.0f : swa_scale;
     const float fs = ks * sm_log2 * qs;
     float lg[16];
+    if (vmask == 0xFFFFFFFFu) {  // a full chunk (most of them): no per-key test
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i / 4) + 4 * hh + (i % 4);
-      lg[i] = ((vmask >> key) & 1u) ? st[i] * fs : -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        float x = st[i] * fs;
+        // the logit is rounded on its own (as the reference maximum is): a fused
+        // multiply-subtract below could land an ulp above the reference, which at
+        // extreme magnitudes is far more than the lazy margin
+        asm("" : "+v"(x));
+        lg[i] = x;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i / 4) + 4 * hh + (i % 4);
+        lg[i] = ((vmask >> key) & 1u) ? st[i] * fs : -INFINITY;
+      }
     }
     // Lazy reference maximum: it only moves (for both lanes of a head) when a
     // logit exceeds it by more than 2^kLazy; everything but the rare rescale of
