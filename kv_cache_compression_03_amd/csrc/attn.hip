@@ -404,14 +404,27 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   for (int d4 = tid; d4 < D / 4; d4 += 128) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < n_splits; ++s) {
-      const float ws = wgt[s];
-      if (ws != 0.0f) {
-        const float4 v = reinterpret_cast<const float4*>(part_o + (base + (size_t)s * H_q) * D)[d4];
-        acc.x += v.x * ws;
-        acc.y += v.y * ws;
-        acc.z += v.z * ws;
-        acc.w += v.w * ws;
+    // splits in batches whose loads are all in flight together (one memory round
+    // trip per batch rather than per split); summed in split order
+    constexpr int BATCH = 8;
+    for (int s0 = 0; s0 < n_splits; s0 += BATCH) {
+      float4 v[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int s = s0 + u;
+        v[u] = s < n_splits ? reinterpret_cast<const float4*>(part_o + (base + (size_t)s * H_q) * D)[d4]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int s = s0 + u;
+        const float ws = s < n_splits ? wgt[s] : 0.0f;
+        if (ws != 0.0f) {
+          acc.x += v[u].x * ws;
+          acc.y += v[u].y * ws;
+          acc.z += v[u].z * ws;
+          acc.w += v[u].w * ws;
+        }
       }
     }
     reinterpret_cast<float4*>(out + ((size_t)row * H_q + h) * D)[d4] =

@@ -543,13 +543,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_row_kernel(
   __syncthreads();
   int slot = x - cnt;
   for (int w2 = 0; w2 < wave; ++w2) slot += wsum[w2];
+  // the chosen indices in ascending order, in LDS (chosen[] was last read before
+  // the bitmap barrier), then one parallel pass maps them through the candidate
+  // map and stores them: one memory round trip, not one per chosen index
+  for (uint32_t m = word; m; m &= m - 1u) chosen[slot++] = 32 * tid + __ffs(m) - 1;
+  __syncthreads();
   int* orow = out + (size_t)r * K;
   const int* cmap_row = cand_map ? cand_map + (size_t)r * N : nullptr;
-  for (uint32_t m = word; m; m &= m - 1u) {
-    const int v = 32 * tid + __ffs(m) - 1;
-    orow[slot++] = cmap_row ? cmap_row[v] : v;
+  for (int i = tid; i < K; i += kSelThreads) {
+    const int v = i < k ? chosen[i] : -1;
+    orow[i] = (cmap_row != nullptr && v >= 0) ? cmap_row[v] : v;
   }
-  for (int i = k + tid; i < K; i += kSelThreads) orow[i] = -1;
 }
 
 hipError_t launch_topk(const float* scores, int R, int N, const int* valid_len, const int* cand_map,

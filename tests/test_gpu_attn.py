@@ -65,6 +65,8 @@ def compare_lse(lse, q, codes, scales, sel, swa, swa_scale=1.0, q_pos=None, swa_
     (2, 32, 256, 2048, 300, 77, None),      # d = 256, one 32-head group, ragged window
     (2, 96, 512, 3000, 512, 128, None),     # three 32-head workgroups per split
     (2, 48, 512, 3000, 512, 128, None),     # H_q not a multiple of 32: bf16 kernel
+    (2, 64, 512, 5000, 2048, 128, None),    # 68 chunks per row: split-K fp16 kernel + combine
+    (1, 64, 512, 5000, 896, 128, 700),      # 32 chunks per row: the two-pass limit
 ])
 def test_decode_attention(B, H, d, N, K, S, n_sel):
     rng = np.random.default_rng(N + H + d)
