@@ -24,7 +24,7 @@ constexpr int kScanWaves = 4;
 #define CSA2_SCAN_BATCH 2
 #endif
 #ifndef CSA2_SCAN_TARGET_WGS
-#define CSA2_SCAN_TARGET_WGS 16384
+#define CSA2_SCAN_TARGET_WGS 65536
 #endif
 constexpr int kScanBatch = CSA2_SCAN_BATCH;  // entry tiles whose keys are in flight together
 
