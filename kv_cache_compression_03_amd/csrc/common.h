@@ -131,15 +131,41 @@ CSA2_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" :
 
 // ---------------------------------------------------------------- wave reductions
 
+// All-lanes reductions without LDS traffic: DPP moves inside each 16-lane row
+// (swap within quads, then rotate the row by 4 and by 8 lanes) leave every lane
+// of a row holding the row's result; one v_readlane per row and three scalar
+// steps finish.  (A __shfl_xor butterfly is six ds_bpermute round trips.)  Every
+// lane of the wave must be active.
+template <int CTRL>
+CSA2_DEV int dpp_mov(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;  // row_ror:4
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8
+template <typename Op>
+CSA2_DEV int wave_reduce_i32(int v, Op op) {
+  v = op(v, dpp_mov<kDppQuadXor1>(v));
+  v = op(v, dpp_mov<kDppQuadXor2>(v));
+  v = op(v, dpp_mov<kDppRowRor4>(v));
+  v = op(v, dpp_mov<kDppRowRor8>(v));
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return op(op(a, b), op(c, d));
+}
 CSA2_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return __int_as_float(wave_reduce_i32(__float_as_int(v), [](int x, int y) {
+    return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y)));
+  }));
 }
 CSA2_DEV float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
+  return __int_as_float(wave_reduce_i32(__float_as_int(v), [](int x, int y) {
+    return __float_as_int(fminf(__int_as_float(x), __int_as_float(y)));
+  }));
+}
+CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
+  return (uint32_t)wave_reduce_i32((int)v, [](int x, int y) { return (int)max((uint32_t)x, (uint32_t)y); });
 }
 CSA2_DEV unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll

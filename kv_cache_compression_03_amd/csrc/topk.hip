@@ -644,11 +644,6 @@ __global__ __launch_bounds__(256) void pool_blockmax_kernel(const float* __restr
   }
 }
 
-CSA2_DEV uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
 
 // Per selected block, its PE best entries (score, then lower index) in ascending
 // index order.  One wave per block, KPL = ceil(G/64) keys per lane; each pick is
@@ -713,7 +708,7 @@ __global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restric
   int rank = 0;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const int v = __shfl(mine, q);
+    const int v = __builtin_amdgcn_readlane(mine, q);
     rank += (q < cntb && v < mine) ? 1 : 0;
   }
   if (lane < cntb) prow[(size_t)slot * PE + rank] = mine;
