@@ -265,13 +265,17 @@ CSA2_DEV void radix_select_row(const float* __restrict__ row, int n, int k, int*
 // The k-th largest of `total` unique 64-bit keys in LDS, by 8-bit digits; the bits
 // every key shares (scores of one magnitude share their top bits) are skipped, so
 // the first digit already spreads the keys.  Stops early once a digit's bucket is
-// taken whole.  Returns T such that exactly k keys are >= T.
+// taken whole.  Returns T such that exactly k keys are >= T.  hist holds two
+// 256-bucket histograms and bcast eight slots: pass p counts into histogram p%2
+// and publishes in slots 3(p%2) .. +2 while the other histogram is cleared for
+// the next pass, so a pass needs two barriers.
 CSA2_DEV unsigned long long radix_kth_u64(const unsigned long long* keys, int total, int k,
                                           uint32_t* hist, unsigned long long* bcast) {
   const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 256) hist[tid] = 0u;
   if (tid == 0) {
-    bcast[2] = 0ull;
-    bcast[3] = ~0ull;
+    bcast[6] = 0ull;
+    bcast[7] = ~0ull;
   }
   __syncthreads();
   // common high bits: OR and AND of all keys agree exactly where every key agrees
@@ -280,38 +284,42 @@ CSA2_DEV unsigned long long radix_kth_u64(const unsigned long long* keys, int to
     kor |= keys[i];
     kand &= keys[i];
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kor |= __shfl_xor(kor, o);
-    kand &= __shfl_xor(kand, o);
-  }
-  if (lane == 0) {
-    atomicOr(reinterpret_cast<unsigned long long*>(&bcast[2]), kor);
-    atomicAnd(reinterpret_cast<unsigned long long*>(&bcast[3]), kand);
+  {
+    auto bor = [](int x, int y) { return x | y; };
+    auto band = [](int x, int y) { return x & y; };
+    const uint32_t oh = (uint32_t)wave_reduce_i32((int)(kor >> 32), bor);
+    const uint32_t ol = (uint32_t)wave_reduce_i32((int)(uint32_t)kor, bor);
+    const uint32_t ah = (uint32_t)wave_reduce_i32((int)(kand >> 32), band);
+    const uint32_t al = (uint32_t)wave_reduce_i32((int)(uint32_t)kand, band);
+    if (lane == 0) {
+      atomicOr(&bcast[6], ((unsigned long long)oh << 32) | ol);
+      atomicAnd(&bcast[7], ((unsigned long long)ah << 32) | al);
+    }
   }
   __syncthreads();
-  const unsigned long long diff = bcast[2] ^ bcast[3];
+  const unsigned long long diff = bcast[6] ^ bcast[7];
   const int top = diff ? 63 - __clzll(diff) : 0;  // highest bit where keys differ
   unsigned long long mask = diff ? ~0ull << (top + 1) : ~0ull;
   if (top == 63) mask = 0ull;
-  unsigned long long prefix = bcast[3] & mask;
+  unsigned long long prefix = bcast[7] & mask;
   int need = k;
-  __syncthreads();
-  for (int shift = top - 7; shift > -8; shift -= 8) {
+  int pass = 0;
+  for (int shift = top - 7; shift > -8; shift -= 8, ++pass) {
     if (shift < 0) shift = 0;
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
+    uint32_t* h = hist + 256 * (pass & 1);
+    if (tid < 256) hist[256 * ((pass + 1) & 1) + tid] = 0u;  // the next pass's histogram
     for (int i = tid; i < total; i += kSelThreads) {
       const unsigned long long key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+      if ((key & mask) == prefix) atomicAdd(&h[(uint32_t)(key >> shift) & 255u], 1u);
     }
     __syncthreads();
+    unsigned long long* bc = bcast + 3 * (pass & 1);
     if (tid < 64) {
       // lane l owns buckets 4l..4l+3; find the bucket where the count from the top reaches need
-      uint32_t h[4];
+      uint32_t hv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = hist[4 * lane + q];
-      const int c = (int)(h[0] + h[1] + h[2] + h[3]);
+      for (int q = 0; q < 4; ++q) hv[q] = h[4 * lane + q];
+      const int c = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
       int suf = c;  // inclusive suffix over lanes
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -321,18 +329,17 @@ CSA2_DEV unsigned long long radix_kth_u64(const unsigned long long* keys, int to
       int run = suf - c;  // keys in buckets above this lane's
 #pragma unroll
       for (int q = 3; q >= 0; --q) {
-        if (run < need && run + (int)h[q] >= need) {
-          bcast[0] = (unsigned long long)(4 * lane + q);
-          bcast[1] = (unsigned long long)(need - run);
-          bcast[2] = (unsigned long long)h[q];
+        if (run < need && run + (int)hv[q] >= need) {
+          bc[0] = (unsigned long long)(4 * lane + q);
+          bc[1] = (unsigned long long)(need - run);
+          bc[2] = (unsigned long long)hv[q];
         }
-        run += (int)h[q];
+        run += (int)hv[q];
       }
     }
     __syncthreads();
-    const unsigned long long dsel = bcast[0];
-    const int need2 = (int)bcast[1], bucket = (int)bcast[2];
-    __syncthreads();
+    const unsigned long long dsel = bc[0];
+    const int need2 = (int)bc[1], bucket = (int)bc[2];
     prefix = (prefix & ~(255ull << shift)) | (dsel << shift);
     mask |= 255ull << shift;
     need = need2;
@@ -377,8 +384,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ cscore, const int* __restrict__ cidx) {
   extern __shared__ unsigned long long keys[];  // kTopkCap keys (64 KB)
   __shared__ __attribute__((aligned(16))) int chosen[2048];
-  __shared__ uint32_t hist[256];
-  __shared__ unsigned long long bcast[4];
+  __shared__ uint32_t hist[512];
+  __shared__ unsigned long long bcast[8];
   __shared__ int misc[32];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n = row_len(valid_len, r, N);
@@ -429,13 +436,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
 // radix select as for short rows.  A row whose candidates overflow (heavy ties)
 // falls back to the exact whole-row select.
 
-__global__ __launch_bounds__(kSelThreads) void topk_row_kernel(
+// Two rows per CU (eight waves per SIMD) are part of the design, and the bound
+// keeps the register budget there: without it the compiler used 85 scalar
+// registers and the GPU then held only one row per CU (prefill rows 1.8x
+// slower); with it a few scalar registers spill to vector lanes.
+__global__ __launch_bounds__(kSelThreads, 8) void topk_row_kernel(
     const float* __restrict__ scores, int N, const int* __restrict__ valid_len,
     const int* __restrict__ cand_map, int K, int* __restrict__ out) {
   __shared__ unsigned long long keys[kTopkCap];   // 64 KB
   __shared__ __attribute__((aligned(16))) int chosen[2048];
-  __shared__ uint32_t hist[256];
-  __shared__ unsigned long long bcast[4];
+  __shared__ uint32_t hist[512];
+  __shared__ unsigned long long bcast[8];
   __shared__ int misc[32];
   __shared__ float red[kSelThreads / 64];
   __shared__ uint32_t bitmap[kRowCap / 32];
@@ -494,16 +505,25 @@ __global__ __launch_bounds__(kSelThreads) void topk_row_kernel(
 #pragma unroll
     for (int w2 = 1; w2 < kSelThreads / 64; ++w2) T = fminf(T, red[w2]);
     const uint32_t tk = mono_key(T);
+    // the wave's candidates of all kPer rounds take one slot range (one atomic);
+    // the ballots are taken again for the placement rather than kept (sixteen
+    // 64-bit masks in scalar registers would cost the second workgroup per CU)
+    int wcnt = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      wcnt += __popcll(__ballot(tid + u * kSelThreads < n && mono_key(rv[u]) >= tk));
+    int wpos = 0;
+    if (lane == 0 && wcnt) wpos = atomicAdd(&misc[0], wcnt);
+    wpos = __builtin_amdgcn_readfirstlane(wpos);
+    const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = tid + u * kSelThreads;
       const bool take = i < n && mono_key(rv[u]) >= tk;
       const unsigned long long m = __ballot(take);
-      int wpos = 0;
-      if (lane == 0 && m) wpos = atomicAdd(&misc[0], __popcll(m));
-      wpos = __shfl(wpos, 0);
-      const int pos = wpos + __popcll(m & ((1ull << lane) - 1ull));
+      const int pos = wpos + __popcll(m & below);
       if (take && pos < kTopkCap) keys[pos] = make_key(rv[u], i);
+      wpos += __popcll(m);
     }
     __syncthreads();
     total = misc[0];
