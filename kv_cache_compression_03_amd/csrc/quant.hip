@@ -62,7 +62,7 @@ hipError_t launch_quant_fp4(const float* kv, long long n, int d, uint8_t* codes,
 
 // ------------------------------------------------------------------ indexer key
 
-constexpr int kIkEntries = 32;  // entries per workgroup
+constexpr int kIkEntries = 16;  // entries per workgroup
 
 template <int DI>
 __global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restrict__ codes,
@@ -96,10 +96,25 @@ __global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restric
   double acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) acc[p] = 0.0;
-  for (int k = 0; k < d; ++k) {
-    const double wv = (double)bf16_to_f32(W[(size_t)k * DI + c]);
+  // weights 16 rows at a time, the next 16 in flight during this block's FMAs
+  // (one load per step would wait on a memory round trip every step); the sum
+  // still runs over k in order
+  constexpr int KB = 16;  // d is a multiple of 32
+  uint32_t wb[KB], wn[KB];
 #pragma unroll
-    for (int p = 0; p < PER; ++p) acc[p] = fma((double)xs[(grp + p * GRP) * d + k], wv, acc[p]);
+  for (int kk = 0; kk < KB; ++kk) wb[kk] = W[(size_t)kk * DI + c];
+  for (int k0 = 0; k0 < d; k0 += KB) {
+    const int kn = k0 + KB < d ? k0 + KB : k0;
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) wn[kk] = W[(size_t)(kn + kk) * DI + c];
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const double wv = (double)bf16_to_f32(wb[kk]);
+#pragma unroll
+      for (int p = 0; p < PER; ++p) acc[p] = fma((double)xs[(grp + p * GRP) * d + k0 + kk], wv, acc[p]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) wb[kk] = wn[kk];
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
