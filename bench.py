@@ -57,6 +57,39 @@ def source_sha(*names) -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_record(name, *sources):
+    """HBM bytes per launch from a committed counter summary under profiles/, or
+    None when there is none or it was taken on other kernel sources."""
+    tf = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(tf):
+        return None
+    rec = {}
+    with open(tf) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                rec[k.strip()] = v.strip()
+    # counters taken on an older kernel source no longer describe this one
+    if rec.get("source_sha") != source_sha(*sources):
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def copy_calibration(args, torch):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters of the same profiled command."""
+    if not args.copy_calibration_mib:
+        return
+    n = args.copy_calibration_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {n} bytes read, {n} bytes written")
+    del src, dst
+
+
 def algorithmic_bytes(wl) -> dict:
     """Bytes a step must move at least: every Full layer streams the indexer keys
     of all entries; a Reindex layer gathers the keys of its pool; every layer reads
@@ -197,6 +230,7 @@ def prefill_main(args, wl, torch, bd, sch):
     log(f"prefill inputs built: {Tq} queries, {len(layers)} layers")
     run = sch.PrefillChunk(wl.layers, N, n_pre, Tq, d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K, wl.m,
                            wl.pos0, wl.swa_pos0, wl.n_win, wl.rope_dim)
+    copy_calibration(args, torch)
     step = lambda: run.step(H, Wkv, Wz, Wik, codes, scales, kidx, layers)
     if not args.no_graph:
         s = torch.cuda.Stream()
@@ -233,6 +267,7 @@ def prefill_main(args, wl, torch, bd, sch):
     idx_s = e0.elapsed_time(e1) / args.kernel_reps / 1e3
     fl = prefill_flops(wl)
     achieved = fl["indexer"] / idx_s / 1e12
+    traffic = traffic_record(f"traffic_index_prefill_{wl.name}.txt", "index_prefill.hip", "common.h")
     log(f"indexer: {idx_s * 1e6:.1f} us/launch, {achieved:.1f} TFLOP/s")
     out = {
         "metric": "CSA2 prefill chunk tokens/s; indexer MFMA TFLOP/s vs MI355X bf16 peak",
@@ -254,7 +289,7 @@ def prefill_main(args, wl, torch, bd, sch):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "indexer scoring (causal Q·K^T, bf16)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic,
                      "launch_us": idx_s * 1e6, "algorithmic_flops_per_launch": fl["indexer"]},
         "chunk_flops": fl,
     }
@@ -284,15 +319,7 @@ def main():
         raise SystemExit("workloads built from hidden states are parity cases, not bench lines")
     log(f"workload {wl.name}: B={wl.B} N={wl.N} d={wl.d} schedule={wl.schedule}")
     codes, scales, kidx, layers = build_inputs(wl, torch, bd, sch)
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {n} bytes read, {n} bytes written")
-        del src, dst
+    copy_calibration(args, torch)
     run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
                              G=wl.G, PB=wl.PB, PE=wl.PE)
     if args.no_graph:
@@ -322,18 +349,7 @@ def main():
     achieved = scan_bytes / scan_s / 1e9
     log(f"scan kernel: {scan_s * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
 
-    traffic = None
-    tf = os.path.join(ROOT, "profiles", f"traffic_index_scores_{wl.name}.txt")
-    if os.path.exists(tf):
-        rec = {}
-        with open(tf) as f:
-            for line in f:
-                if "=" in line and not line.lstrip().startswith("#"):
-                    k, v = line.split("=", 1)
-                    rec[k.strip()] = v.strip()
-        # counters taken on an older kernel source no longer describe this one
-        if rec.get("source_sha") == source_sha("index.hip", "common.h"):
-            traffic = int(rec["hbm_bytes_per_launch"])
+    traffic = traffic_record(f"traffic_index_scores_{wl.name}.txt", "index.hip", "common.h")
 
     out = {
         "metric": METRIC,
