@@ -35,7 +35,8 @@ static inline int xcd_grid(int rows, int per_row) {
   return rows < 8 ? rows * per_row : 8 * ((rows + 7) / 8) * per_row;
 }
 
-// fp16 kernel (attn_f16.hip): 32-head groups, whole selection of a split staged.
+// fp16 kernel (attn_f16.hip): 32-head groups, whole selection of a split staged;
+// hg2 = 32-head groups per workgroup (1 or 2, H_q / 32 a multiple of hg2).
 // Usable when H_q is a multiple of 32, d is 256 or 512 and 0 < swa_scale <= 128
 // (probabilities times the window scale stay inside fp16 range and are formed as
 // one power of two).
@@ -44,7 +45,7 @@ hipError_t launch_sparse_attn_f16(const uint16_t* q, const uint8_t* codes, const
                                   int N, const int* sel, int K, const uint8_t* swa, float swa_scale,
                                   int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,
                                   int H_q, int d, float sm_log2, const AttnPlan& p, int rows,
-                                  float* part_o, float* part_ml, float* out, float* lse,
+                                  int hg2, float* part_o, float* part_ml, float* out, float* lse,
                                   hipStream_t st);
 
 }  // namespace csa2

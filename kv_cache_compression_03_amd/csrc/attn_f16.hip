@@ -460,9 +460,8 @@ hipError_t launch_sparse_attn_f16(const uint16_t* q, const uint8_t* codes, const
                                   int N, const int* sel, int K, const uint8_t* swa, float swa_scale,
                                   int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,
                                   int H_q, int d, float sm_log2, const AttnPlan& p, int rows,
-                                  float* part_o, float* part_ml, float* out, float* lse,
+                                  int hg2, float* part_o, float* part_ml, float* out, float* lse,
                                   hipStream_t st) {
-  const int hg2 = (H_q / 32) % 2 == 0 ? 2 : 1;
   const int head_groups = H_q / (32 * hg2);
   dim3 grid(xcd_grid(rows, p.n_splits * head_groups));
 #define CSA2_ATTN16(D_, HG_)                                                                      \
