@@ -103,6 +103,31 @@ CSA2_API int csa2_quant_fp4(const float* kv, long long n, int d, uint8_t* codes,
                             const void* W_ik, int d_i, void* k_idx, void* stream);
 
 /*
+ * csa2_cache_append -- decode-step cache append: one new Main-KV entry per
+ * sequence into row `row` of each sequence's FP4 cache (with its indexer key),
+ * and the new token's window KV into slot `slot` of each layer's window.
+ * [deep-dive §3.1] the compressor's entries become FP4 Main KV after RoPE
+ * (§3.4) with the indexer K projected from them; [reading §4.2] every layer
+ * keeps its own window of recent tokens, FP8 [deep-dive §3.4].  Quantisation
+ * and key exactly as csa2_quant_fp4; window codes = E4M3(float32(win /
+ * swa_scale)), nearest-even, saturating at 448, sign kept.
+ *   kv     [B, d] f32: the new entries (from csa2_compress), or NULL when this
+ *          token completes no entry (m > 1)
+ *   codes  [B, cap, d/2], scales [B, cap, d/16]: the caches; entry b goes to
+ *          row b * cap + row
+ *   W_ik   [d, d_i] bf16 and k_idx [B, cap, d_i] bf16, or both NULL
+ *   win    [L, B, d] f32: the token's window KV for L window buffers (L = 0: none)
+ *   swa    [L, B, S, d] u8 E4M3: the windows; 0 <= slot < S (a ring: position mod S;
+ *          attention without query positions reads every window token, in any order)
+ * Other rows and slots are left untouched.  Limits as csa2_quant_fp4; the buffers
+ * 16-byte aligned.  Calls that write the same rows concurrently race.
+ */
+CSA2_API int csa2_cache_append(const float* kv, int B, int d, long long cap, long long row,
+                               uint8_t* codes, uint8_t* scales, const void* W_ik, int d_i,
+                               void* k_idx, const float* win, int L, int S, int slot,
+                               float swa_scale, uint8_t* swa, void* stream);
+
+/*
  * csa2_index_full -- Full-mode indexer: score every visible entry, and (first
  * Full layer of a decode step) build the shared candidate pool.
  * [deep-dive §3.1, §3.2] Indexer Q x Indexer K -> score;  reading: for query t,

@@ -30,6 +30,8 @@ _SIGS = {
     "csa2_compress": ([_c_p, _c_i, _c_i, _c_i, _c_i, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_ll,
                        _c_i, _c_d, _c_p, _c_p], _c_i),
     "csa2_quant_fp4": ([_c_p, _c_ll, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_p], _c_i),
+    "csa2_cache_append": ([_c_p, _c_i, _c_i, _c_ll, _c_ll, _c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_i,
+                           _c_i, _c_i, _c_f, _c_p, _c_p], _c_i),
     "csa2_index_full_workspace": ([_c_i, _c_i, _c_i, _c_i, _c_i, _c_i], _c_sz),
     "csa2_index_full": ([_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_p, _c_i, _c_p, _c_p,
                          _c_p, _c_i, _c_i, _c_i, _c_p, _c_sz, _c_p], _c_i),
@@ -182,6 +184,35 @@ def csa2_quant_fp4(kv, codes=None, scales=None, W_ik=None, k_idx=None, stream=No
     _call("csa2_quant_fp4", _p(kv), n, d, _p(codes), _p(scales), _p(W_ik), d_i, _p(k_idx),
           _stream(stream))
     return (codes, scales) if W_ik is None else (codes, scales, k_idx)
+
+
+def csa2_cache_append(codes, scales, row: int, kv=None, W_ik=None, k_idx=None, win=None, swa=None,
+                      slot: int = 0, swa_scale: float = 1.0, stream=None) -> None:
+    """Decode cache append.  codes [B, cap, d/2], scales [B, cap, d/16] (and k_idx
+    [B, cap, d_i] with W_ik [d, d_i]) receive kv [B, d] f32 in row `row`; swa
+    [L, B, S, d] E4M3 bytes receive win [L, B, d] f32 in slot `slot`."""
+    _dev(codes, "codes", U8)
+    _dev(scales, "scales", U8)
+    B, cap = codes.shape[0], codes.shape[1]
+    d = codes.shape[2] * 2
+    if kv is not None:
+        _dev(kv, "kv", F32)
+        if tuple(kv.shape) != (B, d):
+            raise ValueError(f"kv must be [{B}, {d}]")
+    d_i = 0
+    if W_ik is not None:
+        _dev(W_ik, "W_ik", BF16)
+        _dev(k_idx, "k_idx", BF16)
+        d_i = W_ik.shape[1]
+    L, S = 0, 1
+    if win is not None:
+        _dev(win, "win", F32)
+        _dev(swa, "swa", U8)
+        L, S = swa.shape[0], swa.shape[2]
+        if tuple(win.shape) != (L, B, d) or tuple(swa.shape) != (L, B, S, d):
+            raise ValueError("win must be [L, B, d] and swa [L, B, S, d]")
+    _call("csa2_cache_append", _p(kv), B, d, cap, row, _p(codes), _p(scales), _p(W_ik), d_i,
+          _p(k_idx), _p(win), L, S, slot, float(swa_scale), _p(swa), _stream(stream))
 
 
 def csa2_index_full(q_idx, w, k_idx, q_pos=None, m: int = 1, scores=None, pool=None, pool_len=None,

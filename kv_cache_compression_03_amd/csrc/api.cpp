@@ -125,6 +125,50 @@ CSA2_API int csa2_quant_fp4(const float* kv, long long n, int d, uint8_t* codes,
   return hip_status(e, fn);
 }
 
+// ------------------------------------------------------------------ decode cache append
+
+CSA2_API int csa2_cache_append(const float* kv, int B, int d, long long cap, long long row,
+                               uint8_t* codes, uint8_t* scales, const void* W_ik, int d_i,
+                               void* k_idx, const float* win, int L, int S_, int slot,
+                               float swa_scale, uint8_t* swa, void* stream) {
+  const char* fn = "csa2_cache_append";
+  CHECK(B >= 0 && L >= 0, CSA2_ERR_INVALID_ARG, "%s: negative size", fn);
+  CHECK(d > 0 && d % 32 == 0 && d <= 1024, CSA2_ERR_UNSUPPORTED, "%s: d must be a multiple of 32 in [32, 1024]", fn);
+  CHECK((W_ik == nullptr) == (k_idx == nullptr), CSA2_ERR_INVALID_ARG,
+        "%s: W_ik and k_idx must both be given or both be null", fn);
+  if (W_ik) {
+    CHECK(d_i == 64 || d_i == 128, CSA2_ERR_UNSUPPORTED, "%s: d_i must be 64 or 128", fn);
+    CHECK(d <= 512, CSA2_ERR_UNSUPPORTED, "%s: the indexer-key projection needs d <= 512", fn);
+  }
+  if (kv) CHECK(cap >= 1 && row >= 0 && row < cap, CSA2_ERR_INVALID_ARG, "%s: row must be in [0, cap)", fn);
+  if (L > 0) {
+    CHECK(S_ >= 1 && slot >= 0 && slot < S_, CSA2_ERR_INVALID_ARG, "%s: slot must be in [0, S)", fn);
+    CHECK(std::isfinite(swa_scale) && swa_scale > 0.0f, CSA2_ERR_INVALID_ARG,
+          "%s: swa_scale must be finite and > 0", fn);
+  }
+  if (B == 0) return ok();
+  OPT_PTR(kv);
+  OPT_PTR(W_ik);
+  OPT_PTR(k_idx);
+  if (kv) {
+    NEED_PTR(codes);
+    NEED_PTR(scales);
+  }
+  if (L > 0) {
+    NEED_PTR(win);
+    NEED_PTR(swa);
+  }
+  hipError_t e = hipSuccess;
+  if (kv) {
+    e = csa2::launch_quant_fp4(kv, B, d, codes, scales, S(stream), cap, row);
+    if (e == hipSuccess && W_ik)
+      e = csa2::launch_indexer_k(codes, scales, B, d, static_cast<const uint16_t*>(W_ik), d_i,
+                                 static_cast<uint16_t*>(k_idx), S(stream), cap, row);
+  }
+  if (e == hipSuccess && L > 0) e = csa2::launch_swa_append(win, L, B, S_, d, slot, swa_scale, swa, S(stream));
+  return hip_status(e, fn);
+}
+
 // ------------------------------------------------------------------ Full-mode indexer
 
 static bool index_dims_ok(int h_i, int d_i) {

@@ -11,10 +11,15 @@ namespace csa2 {
 constexpr int kTopkCap = 8192;  // candidates a Top-K row sorts in LDS
 
 // quant.hip
+// Entry e of the input goes to cache row e * cap + row (defaults: contiguous).
 hipError_t launch_quant_fp4(const float* kv, long long n, int d, uint8_t* codes, uint8_t* scales,
-                            hipStream_t st);
+                            hipStream_t st, long long cap = 1, long long row = 0);
 hipError_t launch_indexer_k(const uint8_t* codes, const uint8_t* scales, long long n, int d,
-                            const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st);
+                            const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st,
+                            long long cap = 1, long long row = 0);
+// win [L, B, d] f32 -> E4M3 codes of win / swa_scale in swa[l][b][slot] ([L, B, S, d]).
+hipError_t launch_swa_append(const float* win, int L, int B, int S, int d, int slot, float swa_scale,
+                             uint8_t* swa, hipStream_t st);
 
 // compress.hip
 hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_model, const void* W_kv,

@@ -11,20 +11,28 @@
 //        contiguous.  fp32 divisions are IEEE correctly rounded (built with
 //        -fhip-fp32-correctly-rounded-divide-sqrt), which makes the codes
 //        bit-identical to any other correct implementation of the same rule.
-// indexer_k: 32 entries per workgroup are dequantised into LDS (fp32, exact),
+// indexer_k: 16 entries per workgroup are dequantised into LDS (fp32, exact),
 //        then each thread accumulates one key channel of several entries in
 //        float64 and rounds once to bf16.
+// Both place entry e of their input at cache row e * cap + row (cap = 1, row = 0:
+// contiguous), so a decode step can write one new entry per sequence into row n
+// of a [B, cap, ...] cache.
+// swa_append: one thread per 16 values of a new token's window KV, E4M3 codes
+//        into one slot of each window buffer.
 #include "common.h"
 #include "internal.h"
 
 namespace csa2 {
 
 __global__ __launch_bounds__(256) void quant_fp4_kernel(const float* __restrict__ kv,
-                                                        long long ngroups,
+                                                        long long ngroups, int gpe, long long cap,
+                                                        long long row,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales) {
   long long g = (long long)blockIdx.x * 256 + threadIdx.x;
   if (g >= ngroups) return;
+  const long long e = g / gpe;
+  const long long go = (e * cap + row) * gpe + (g - e * gpe);  // output group
   const float4* src = reinterpret_cast<const float4*>(kv) + g * 4;
   float x[16];
 #pragma unroll
@@ -46,17 +54,17 @@ __global__ __launch_bounds__(256) void quant_fp4_kernel(const float* __restrict_
     uint32_t c = s > 0.0f ? e2m1_encode(x[i] / s) : ((__float_as_uint(x[i]) >> 28) & 8u);
     w[i >> 3] |= c << (4 * (i & 7));
   }
-  reinterpret_cast<uint2*>(codes)[g] = make_uint2(w[0], w[1]);
-  scales[g] = (uint8_t)S;
+  reinterpret_cast<uint2*>(codes)[go] = make_uint2(w[0], w[1]);
+  scales[go] = (uint8_t)S;
 }
 
 hipError_t launch_quant_fp4(const float* kv, long long n, int d, uint8_t* codes, uint8_t* scales,
-                            hipStream_t st) {
+                            hipStream_t st, long long cap, long long row) {
   long long ngroups = n * (d / 16);
   if (ngroups == 0) return hipSuccess;
   long long blocks = (ngroups + 255) / 256;
-  hipLaunchKernelGGL(quant_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, kv, ngroups, codes,
-                     scales);
+  hipLaunchKernelGGL(quant_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, kv, ngroups, d / 16,
+                     cap, row, codes, scales);
   return hipGetLastError();
 }
 
@@ -67,7 +75,8 @@ constexpr int kIkEntries = 16;  // entries per workgroup
 template <int DI>
 __global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ scales,
-                                                        long long n, int d,
+                                                        long long n, int d, long long cap,
+                                                        long long row,
                                                         const uint16_t* __restrict__ W,
                                                         uint16_t* __restrict__ out) {
   extern __shared__ float xs[];  // [kIkEntries][d]
@@ -75,11 +84,11 @@ __global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restric
   const int slabs = d / 8;
   for (int t = threadIdx.x; t < kIkEntries * slabs; t += 256) {
     const int el = t / slabs, sl = t - el * slabs;
-    const long long e = e0 + el;
+    const long long e = e0 + el, r = e * cap + row;
     float v[8];
     if (e < n) {
-      uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + e * (d / 2) + sl * 4);
-      float s = e4m3_decode(scales[e * (d / 16) + (sl >> 1)]);
+      uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + r * (d / 2) + sl * 4);
+      float s = e4m3_decode(scales[r * (d / 16) + (sl >> 1)]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((cw >> (4 * j)) & 15u) * s;
     } else {
@@ -119,21 +128,62 @@ __global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restric
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const long long e = e0 + grp + p * GRP;
-    if (e < n) out[e * DI + c] = (uint16_t)f64_to_bf16_rne(acc[p]);
+    if (e < n) out[(e * cap + row) * DI + c] = (uint16_t)f64_to_bf16_rne(acc[p]);
   }
 }
 
 hipError_t launch_indexer_k(const uint8_t* codes, const uint8_t* scales, long long n, int d,
-                            const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st) {
+                            const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st,
+                            long long cap, long long row) {
   if (n == 0) return hipSuccess;
   long long blocks = (n + kIkEntries - 1) / kIkEntries;
   size_t lds = (size_t)kIkEntries * d * sizeof(float);
   if (d_i == 128)
     hipLaunchKernelGGL(indexer_k_kernel<128>, dim3((unsigned)blocks), dim3(256), lds, st, codes,
-                       scales, n, d, W_ik, k_idx);
+                       scales, n, d, cap, row, W_ik, k_idx);
   else
     hipLaunchKernelGGL(indexer_k_kernel<64>, dim3((unsigned)blocks), dim3(256), lds, st, codes,
-                       scales, n, d, W_ik, k_idx);
+                       scales, n, d, cap, row, W_ik, k_idx);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ window append
+
+// win [L, B, d] f32 -> swa[l][b][slot][:] as E4M3 codes of win / swa_scale
+// (nearest-even, saturating at 448, sign kept: -0 -> 0x80).
+__global__ __launch_bounds__(256) void swa_append_kernel(const float* __restrict__ win, long long ngroups,
+                                                         int gpt, int S, int slot, float swa_scale,
+                                                         uint8_t* __restrict__ swa) {
+  long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  const long long tok = g / gpt;  // (layer, sequence)
+  const int gi = (int)(g - tok * gpt);
+  const float4* src = reinterpret_cast<const float4*>(win) + g * 4;
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = src[i];
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float y = x[j] / swa_scale;  // IEEE division (correctly rounded build)
+      const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+      word |= (sign | e4m3_encode_nonneg(fabsf(y))) << (8 * j);
+    }
+    w[i] = word;
+  }
+  reinterpret_cast<uint4*>(swa + ((size_t)tok * S + slot) * (size_t)(gpt * 16))[gi] =
+      make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+hipError_t launch_swa_append(const float* win, int L, int B, int S, int d, int slot, float swa_scale,
+                             uint8_t* swa, hipStream_t st) {
+  const long long ngroups = (long long)L * B * (d / 16);
+  if (ngroups == 0) return hipSuccess;
+  const long long blocks = (ngroups + 255) / 256;
+  hipLaunchKernelGGL(swa_append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, win, ngroups, d / 16,
+                     S, slot, swa_scale, swa);
   return hipGetLastError();
 }
 

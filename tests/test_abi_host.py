@@ -74,6 +74,13 @@ def test_invalid_arguments_rejected_before_launch():
     assert L.csa2_compress(p, 0, 1, 8, 64, p, p, 0, 256, 256, 3, 0, 64, 1e4, p, None) == 2   # m = 3
     assert L.csa2_compress(p, 0, 1, 8, 64, p, p, 1, 256, 256, 2, 0, 64, 1e4, p, None) == 2   # dtypes
     assert L.csa2_compress(p, 0, 1, 8, 64, p, p, 0, 256, 256, 2, 1, 64, 1e4, p, None) == 1   # pos0 % m
+    # cache append: row / slot ranges, window scale, dims
+    assert L.csa2_cache_append(p, 4, 512, 8, 8, p, p, None, 0, None, None, 0, 0, 0, 1.0, None, None) == 1
+    assert b"row" in L.csa2_last_error()
+    assert L.csa2_cache_append(None, 4, 512, 8, 0, p, p, None, 0, None, p, 2, 128, 128, 1.0, p, None) == 1
+    assert L.csa2_cache_append(None, 4, 512, 8, 0, p, p, None, 0, None, p, 2, 128, 3, 0.0, p, None) == 1
+    assert L.csa2_cache_append(None, 4, 40, 8, 0, p, p, None, 0, None, None, 0, 0, 0, 1.0, None, None) == 2
+    assert L.csa2_cache_append(p, 4, 512, 8, 0, p, p, p, 0, None, None, 0, 0, 0, 1.0, None, None) == 1
     # empty work is a no-op success
     assert L.csa2_quant_fp4(None, 0, 512, None, None, None, 0, None, None) == 0
     assert L.csa2_last_error() == b""
