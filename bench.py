@@ -296,6 +296,107 @@ def prefill_main(args, wl, torch, bd, sch):
     print(json.dumps(out), flush=True)
 
 
+def append_main(args, wl, torch, bd):
+    """Decode cache append: one new FP4 entry per sequence (with its indexer key)
+    into row N-1 of each sequence's cache, and the token's window KV into slot
+    (N-1) mod S of all L layer windows; one csa2_cache_append per step, replayed
+    from a graph; inputs resident in HBM.  value = appended tokens / s."""
+    import synth
+    dev = torch.device("cuda")
+    B, d, d_i, L, S, cap = wl.B, wl.d, wl.d_i, len(wl.layers), wl.S, wl.N
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    codes = torch.zeros(B, cap, d // 2, dtype=torch.uint8, device=dev)
+    scales = torch.zeros(B, cap, d // 16, dtype=torch.uint8, device=dev)
+    kidx = torch.zeros(B, cap, d_i, dtype=torch.bfloat16, device=dev)
+    swa = torch.zeros(L, B, S, d, dtype=torch.uint8, device=dev)
+    W = bf(synth.w_ik(wl))
+    kv_h = np.stack([synth.main_kv(wl, b, cap - 1, cap)[0] for b in range(B)])
+    win_h = synth.new_token_window(wl)
+    kv, win = torch.from_numpy(kv_h).to(dev), torch.from_numpy(win_h).to(dev)
+    row, slot = cap - 1, (cap - 1) % S
+    log(f"workload {wl.name}: B={B} d={d} d_i={d_i} windows {L} x {S}, row {row}, slot {slot}")
+    step = lambda: bd.csa2_cache_append(codes, scales, row, kv=kv, W_ik=W, k_idx=kidx, win=win, swa=swa,
+                                        slot=slot)
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        step = g.replay
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    step_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    log(f"timed {args.steps} appends: {step_s * 1e6:.1f} us/append")
+    # algorithmic bytes of one call: entries in, W_ik in, codes + scales + keys out,
+    # window KV in, window codes out
+    nbytes = B * d * 4 + d * d_i * 2 + B * (d // 2 + d // 16 + 2 * d_i) + L * B * d * 4 + L * B * d
+    # the compressor at this shape (B sequences x m tokens), for context: its
+    # tiles are sized for prefill (256 tokens), so most of each tile is padding
+    H = bf(synth.append_hidden(wl))
+    Wkv_b, Wz_b = synth.compressor_weights(wl)
+    Wkv, Wz = bf(Wkv_b), bf(Wz_b)
+    kvo = torch.empty(B, 1, d, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        bd.csa2_compress(H, Wkv, Wz, wl.m, pos0=cap * wl.m - wl.m, out=kvo)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.kernel_reps):
+        bd.csa2_compress(H, Wkv, Wz, wl.m, pos0=cap * wl.m - wl.m, out=kvo)
+    e1.record()
+    torch.cuda.synchronize()
+    comp_s = e0.elapsed_time(e1) / 1e3 / args.kernel_reps
+    log(f"compressor at this shape: {comp_s * 1e6:.1f} us")
+    out = {
+        "metric": "CSA2 decode cache append: appended tokens/s; achieved HBM GB/s vs MI355X peak",
+        "value": B / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "sequences": B, "d": d, "indexer_dim": d_i,
+                   "windows": L, "window": S, "graph": not args.no_graph,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "csa2_cache_append (quantise, key, window launches)",
+                     "achieved": nbytes / step_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / step_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "launch_us": step_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
+        "compress_at_this_shape_us": comp_s * 1e6,
+    }
+    if not args.no_cpu_baseline:
+        from oracle.codecs import e4m3_encode
+        from oracle.csa2 import indexer_k, quant_fp4
+        W_h = synth.w_ik(wl)
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            q = quant_fp4(kv_h)
+            indexer_k(q.codes, q.scales, W_h)
+            e4m3_encode(win_h)
+            n += 1
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n * B / el, "unit": "tokens/s", "cores": os.cpu_count(),
+                               "kind": "oracle",
+                               "sample": f"{n} appends of all {B} sequences (quantise, key, window), "
+                                         f"{el:.1f}s, float64 numpy"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -315,6 +416,8 @@ def main():
     wl = synth.workload(args.workload)
     if wl.chunk:
         return prefill_main(args, wl, torch, bd, sch)
+    if wl.append:
+        return append_main(args, wl, torch, bd)
     if wl.T:
         raise SystemExit("workloads built from hidden states are parity cases, not bench lines")
     log(f"workload {wl.name}: B={wl.B} N={wl.N} d={wl.d} schedule={wl.schedule}")

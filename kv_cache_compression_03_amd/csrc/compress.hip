@@ -140,7 +140,7 @@ template <int M>
 __global__ __launch_bounds__(256, 1) void compress_mfma_kernel(
     const uint16_t* __restrict__ H, int T, int d_model, const uint16_t* __restrict__ Wkv,
     const uint16_t* __restrict__ Wz, int d, long long pos0, int rope_dim, double theta, int n_ent,
-    int n_cg, float* __restrict__ out) {
+    int n_cg, int n_per_seq, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t hs[2][kMT * kMP];
   __shared__ __attribute__((aligned(16))) uint16_t wsm[2][2 * kMC * kMP];
   // workgroup -> (token group, channel group); the channel groups of one token
@@ -249,7 +249,9 @@ __global__ __launch_bounds__(256, 1) void compress_mfma_kernel(
           const float other = __shfl_xor(kv, 1);
           if (c >= d - rope_dim) {
             const int i = (c - (d - rope_dim)) >> 1;
-            const double pos = (double)(pos0 + (long long)(ent + 1) * M - 1);
+            // position inside its own sequence (n_per_seq < n_ent when short
+            // sequences were laid end to end)
+            const double pos = (double)(pos0 + (long long)(ent % n_per_seq + 1) * M - 1);
             double sn, cs;
             sincos(pos * pow(theta, -2.0 * i / rope_dim), &sn, &cs);
             const double u = (c & 1) ? other : kv, v = (c & 1) ? kv : other;
@@ -272,12 +274,18 @@ hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_mode
   const int n_ent = T / m;
   if (B == 0 || n_ent == 0) return hipSuccess;
   if (compress_mfma_ok(bf16_in, d_model, d, d_z)) {
-    const int n_tg = (n_ent * m + kMT - 1) / kMT, n_cg = d / kMC;
-    dim3 g2((unsigned)(8 * ((n_tg + 7) / 8) * n_cg), (unsigned)B);
+    // Sequences shorter than a token tile whose tokens all fold (a decode step's
+    // new block per sequence) are laid end to end as one run of B*T tokens: the
+    // rows of [B, T, d_model] are contiguous and blocks never cross a sequence,
+    // so only the RoPE position changes (taken inside each sequence).
+    const bool flat = B > 1 && T % m == 0 && T < kMT;
+    const int Bl = flat ? 1 : B, Tl = flat ? B * T : T, nl = flat ? B * n_ent : n_ent;
+    const int n_tg = (nl * m + kMT - 1) / kMT, n_cg = d / kMC;
+    dim3 g2((unsigned)(8 * ((n_tg + 7) / 8) * n_cg), (unsigned)Bl);
 #define CSA2_COMPM(M_)                                                                                \
   hipLaunchKernelGGL((compress_mfma_kernel<M_>), g2, dim3(256), 0, st, static_cast<const uint16_t*>(H), \
-                     T, d_model, static_cast<const uint16_t*>(W_kv), static_cast<const uint16_t*>(W_z), d, \
-                     pos0, rope_dim, rope_theta, n_ent, n_cg, kv_out)
+                     Tl, d_model, static_cast<const uint16_t*>(W_kv), static_cast<const uint16_t*>(W_z), d, \
+                     pos0, rope_dim, rope_theta, nl, n_cg, n_ent, kv_out)
     if (m == 1) CSA2_COMPM(1);
     else if (m == 2) CSA2_COMPM(2);
     else CSA2_COMPM(4);

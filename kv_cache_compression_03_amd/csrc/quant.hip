@@ -70,9 +70,9 @@ hipError_t launch_quant_fp4(const float* kv, long long n, int d, uint8_t* codes,
 
 // ------------------------------------------------------------------ indexer key
 
-constexpr int kIkEntries = 16;  // entries per workgroup
-
-template <int DI>
+// entries per workgroup: 16, or 2 for small batches (a decode step's new
+// entries), where 16 would leave most of the GPU idle
+template <int DI, int kIkEntries>
 __global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ scales,
                                                         long long n, int d, long long cap,
@@ -136,14 +136,20 @@ hipError_t launch_indexer_k(const uint8_t* codes, const uint8_t* scales, long lo
                             const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st,
                             long long cap, long long row) {
   if (n == 0) return hipSuccess;
-  long long blocks = (n + kIkEntries - 1) / kIkEntries;
-  size_t lds = (size_t)kIkEntries * d * sizeof(float);
-  if (d_i == 128)
-    hipLaunchKernelGGL(indexer_k_kernel<128>, dim3((unsigned)blocks), dim3(256), lds, st, codes,
-                       scales, n, d, cap, row, W_ik, k_idx);
-  else
-    hipLaunchKernelGGL(indexer_k_kernel<64>, dim3((unsigned)blocks), dim3(256), lds, st, codes,
-                       scales, n, d, cap, row, W_ik, k_idx);
+  const int E = n >= 1024 ? 16 : 4;
+  long long blocks = (n + E - 1) / E;
+  size_t lds = (size_t)E * d * sizeof(float);
+#define CSA2_IK(DI_, E_)                                                                      \
+  hipLaunchKernelGGL((indexer_k_kernel<DI_, E_>), dim3((unsigned)blocks), dim3(256), lds, st, codes, \
+                     scales, n, d, cap, row, W_ik, k_idx)
+  if (d_i == 128) {
+    if (E == 16) CSA2_IK(128, 16);
+    else CSA2_IK(128, 4);
+  } else {
+    if (E == 16) CSA2_IK(64, 16);
+    else CSA2_IK(64, 4);
+  }
+#undef CSA2_IK
   return hipGetLastError();
 }
 

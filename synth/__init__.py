@@ -28,7 +28,7 @@ from typing import List, Optional
 import numpy as np
 
 TAG = {"kv": 1, "wik": 2, "qidx": 3, "w": 4, "qmain": 5, "swa": 6, "plant_pos": 7,
-       "plant_dir": 8, "H": 9, "wkv": 10, "wz": 11, "qpos": 12}
+       "plant_dir": 8, "H": 9, "wkv": 10, "wz": 11, "qpos": 12, "winkv": 13, "Happ": 14}
 
 
 @dataclass(frozen=True)
@@ -62,6 +62,9 @@ class Workload:
     # entries come from its hidden states through the compressor
     chunk: int = 0
     n_win: int = 128
+    # decode cache append: one new entry per sequence into row N-1 of an N-row
+    # cache, and the token's window KV into every layer's window
+    append: bool = False
 
     @property
     def pos0(self) -> int:
@@ -105,6 +108,12 @@ WORKLOADS = {
     "prefill_32k": Workload("prefill_32k", B=1, N=16384, d=512, h_i=8, d_i=128, H_q=64,
                             S=8192 + 127, m=2, schedule="FUUUUU", seed=3, T=32768,
                             chunk=8192, d_model=5120, h_dtype="bf16"),
+    # decode cache append: 64 sequences, d = 512 entries with 128-dim keys, the
+    # token's window KV for the 20 decoder layers (128-token windows); the entry
+    # comes from hidden states of width 5,120 (bf16) through the compressor
+    "append_b64": Workload("append_b64", B=64, N=65536, d=512, h_i=8, d_i=128, H_q=64,
+                           schedule="FUUURUUURUUURUUURUUU", seed=5, d_model=5120, h_dtype="bf16",
+                           append=True),
 }
 
 
@@ -229,6 +238,12 @@ def q_positions(wl: Workload) -> np.ndarray:
     return np.arange(wl.pos0, wl.T, dtype=np.int32)
 
 
+def new_token_window(wl: Workload) -> np.ndarray:
+    """Window KV of one new token for every layer and sequence, float32 [L, B, d]."""
+    return np.stack([np.stack([_rng(wl.seed, "winkv", li, b).standard_normal(wl.d, dtype=np.float32)
+                               for b in range(wl.B)]) for li in range(len(wl.layers))])
+
+
 def swa_tokens(wl: Workload, layer: int, b: int, S: Optional[int] = None) -> np.ndarray:
     r = _rng(wl.seed, "swa", layer, b)
     return to_e4m3_codes(r.standard_normal((wl.S if S is None else S, wl.d), dtype=np.float32))
@@ -241,6 +256,14 @@ def hidden(wl: Workload, b: int = 0) -> np.ndarray:
     r = _rng(wl.seed, "H", 0, b)
     h = r.standard_normal((wl.chunk or wl.T, wl.d_model), dtype=np.float32)
     return to_bf16_bits(h) if wl.h_dtype == "bf16" else h
+
+
+def append_hidden(wl: Workload) -> np.ndarray:
+    """Hidden states of the block of m tokens that completes each sequence's new
+    entry (decode cache append), bf16 bits [B, m, d_model]."""
+    h = np.stack([_rng(wl.seed, "Happ", 0, b).standard_normal((wl.m, wl.d_model), dtype=np.float32)
+                  for b in range(wl.B)])
+    return to_bf16_bits(h)
 
 
 def compressor_weights(wl: Workload, d_z: Optional[int] = None):

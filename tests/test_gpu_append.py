@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from helpers import dev, dev_bf16, host_bf16_bits
-from oracle.codecs import e4m3_encode, f64_to_bf16
+from oracle.codecs import bf16_to_f64, e4m3_encode, f64_to_bf16
 from oracle.csa2 import compress, indexer_k, quant_fp4
 from test_gpu_quant import adversarial_kv
 
@@ -71,24 +71,31 @@ def test_window_only_and_entry_only():
     assert np.array_equal(swa.cpu().numpy(), before)
 
 
-@pytest.mark.parametrize("m", [1, 2])
-def test_append_from_hidden_states(m):
+@pytest.mark.parametrize("m,bf16", [(1, False), (2, False), (1, True), (2, True)])
+def test_append_from_hidden_states(m, bf16):
     """Tokens arrive one at a time; whenever a block of m completes, its hidden
     states go through csa2_compress (positions of that block) and the entry is
     appended.  The appended rows match the oracle's compressor over the whole
-    sequence (within one float32 rounding) and the oracle's quantisation of the
-    entries the GPU produced (bit-exact)."""
-    rng = np.random.default_rng(40 + m)
+    sequence (1e-4 of RMS) and the oracle's quantisation of the entries the GPU
+    produced (bit-exact).  bf16 hidden states take the MFMA compressor, which
+    lays the B short sequences end to end (RoPE positions inside each)."""
+    rng = np.random.default_rng(40 + m + 10 * bf16)
     B, T, d_model, d, d_i = 3, 12, 1024, 256, 64
     H = rng.standard_normal((B, T, d_model)).astype(np.float32)
     Wkv = (rng.standard_normal((d_model, d)) / np.sqrt(d_model)).astype(np.float32)
     Wz = (rng.standard_normal((d_model, d)) / np.sqrt(d_model)).astype(np.float32)
+    if bf16:   # inputs rounded to bf16; the oracle reads the same values
+        H, Wkv, Wz = (bf16_to_f64(f64_to_bf16(a)).astype(np.float32) for a in (H, Wkv, Wz))
     W = f64_to_bf16(rng.standard_normal((d, d_i)) / np.sqrt(d))
     cap = T // m
     codes = torch.zeros(B, cap, d // 2, dtype=torch.uint8, device="cuda")
     scales = torch.zeros(B, cap, d // 16, dtype=torch.uint8, device="cuda")
     kidx = torch.zeros(B, cap, d_i, dtype=torch.bfloat16, device="cuda")
-    Hd, Wkvd, Wzd, Wd = dev(H), dev(Wkv), dev(Wz), dev_bf16(W)
+    if bf16:
+        Hd, Wkvd, Wzd = (dev_bf16(f64_to_bf16(a)) for a in (H, Wkv, Wz))
+    else:
+        Hd, Wkvd, Wzd = dev(H), dev(Wkv), dev(Wz)
+    Wd = dev_bf16(W)
     entries = []
     for t in range(T):
         if (t + 1) % m:
