@@ -264,6 +264,123 @@ __global__ __launch_bounds__(256, 1) void compress_mfma_kernel(
   }
 }
 
+// ---- a few tokens (a decode step's new blocks): at most 64 tokens in all
+// (B sequences of T tokens laid end to end).  The prefill kernel gives each
+// workgroup the whole 5,120-deep reduction for 64 channels, which at 64 tokens
+// leaves the GPU nearly idle.  Here a workgroup owns 8 channels (16 MFMA
+// columns: 8 of C, 8 of Z) for every token, and its four waves split the
+// reduction: wave w sums dims [w*d_model/4, (w+1)*d_model/4) into a partial
+// [64 tokens x 16 columns] tile, the four tiles are added through LDS in a fixed
+// order, and the fold and RoPE run as in the prefill kernel (a lane holds 4
+// consecutive tokens of one column; Z of the same channel is 8 lanes away).
+// Per 32-deep step a wave loads its 16 weight columns (16 B per lane: 8 channels
+// of W_KV or of W_Z of one reduction row), transposes them through a private LDS
+// tile and reads its 4 token tiles' A operands straight from global memory; the
+// next step's loads are in flight during this step's MFMAs.
+constexpr int kFewTok = 64;   // tokens per workgroup
+constexpr int kFewCh = 8;     // channels per workgroup
+constexpr int kFewTP = 40;    // LDS pitch (bf16) of a transposed weight column
+
+template <int M>
+__global__ __launch_bounds__(256) void compress_few_kernel(
+    const uint16_t* __restrict__ H, int n_tok, int d_model, const uint16_t* __restrict__ Wkv,
+    const uint16_t* __restrict__ Wz, int d, long long pos0, int rope_dim, double theta,
+    int n_per_seq, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[4][16 * kFewTP];  // per wave: [column][k]
+  __shared__ __attribute__((aligned(16))) float part[4][4 * 64 * 4];     // per wave: 4 tiles x 64 lanes x 4
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
+  const int c0 = blockIdx.x * kFewCh;
+  const int kq = d_model / 4, k_lo = wave * kq;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  // weight loads: lane l = reduction row l/2 of the step, W_KV (l even) or W_Z (odd)
+  const uint16_t* wsrc = ((lane & 1) ? Wz : Wkv) + (size_t)(k_lo + (lane >> 1)) * d + c0;
+  // A rows: token 16 rt + col (clamped: rows past n_tok repeat the last token and are never stored)
+  const uint16_t* hrow[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) hrow[rt] = H + (size_t)min(16 * rt + col, n_tok - 1) * d_model + k_lo + 8 * g;
+  u32x4 wv, ha[4], wv_n, ha_n[4];
+  auto load = [&](int s, u32x4& w, u32x4 (&h)[4]) {
+    w = *reinterpret_cast<const u32x4*>(wsrc + (size_t)s * 32 * d);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) h[rt] = *reinterpret_cast<const u32x4*>(hrow[rt] + 32 * s);
+  };
+  f32x4_t acc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int n_steps = kq / 32;
+  uint16_t* tile = wt[wave];
+  load(0, wv, ha);
+  for (int s = 0; s < n_steps; ++s) {
+    if (s + 1 < n_steps) load(s + 1, wv_n, ha_n);
+    // transpose: column (lane&1)*8 + j gets reduction row lane/2
+    {
+      const uint16_t* v = reinterpret_cast<const uint16_t*>(&wv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[((lane & 1) * 8 + j) * kFewTP + (lane >> 1)] = v[j];
+    }
+    // the wave reads back what it wrote: LDS serves one wave in order; the wait
+    // keeps the compiler from moving the read above the writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&tile[col * kFewTP + 8 * g]);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma16x16x32(as_bf16x8(make_uint4(ha[rt][0], ha[rt][1], ha[rt][2], ha[rt][3])), b, acc[rt]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is rewritten next step
+    if (s + 1 < n_steps) {
+      wv = wv_n;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) ha[rt] = ha_n[rt];
+    }
+  }
+  // ---- the four partial tiles, added in wave order
+  float4* mine = reinterpret_cast<float4*>(part[wave]);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) mine[rt * 64 + lane] = make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]);
+  __syncthreads();
+  // wave w finishes token tile rt = w: lane holds tokens 16w + 4g + i of column col
+  f32x4_t tot;
+  {
+    const float4* p0 = reinterpret_cast<const float4*>(part[0]) + wave * 64 + lane;
+    const float4 a0 = p0[0], a1 = p0[256], a2 = p0[512], a3 = p0[768];
+    tot = f32x4_t{(a0.x + a1.x) + (a2.x + a3.x), (a0.y + a1.y) + (a2.y + a3.y),
+                  (a0.z + a1.z) + (a2.z + a3.z), (a0.w + a1.w) + (a2.w + a3.w)};
+  }
+  // columns 0-7 hold C, 8-15 Z of channels c0 .. c0+7: the Z of this lane's
+  // channel is 8 lanes away
+  f32x4_t zv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zv[i] = __shfl_xor(tot[i], 8);
+  const bool is_c = col < 8;
+  const int c = c0 + (col & 7);
+  const int t0 = 16 * wave + 4 * g;
+#pragma unroll
+  for (int e = 0; e < 4 / M; ++e) {
+    float zmax = zv[e * M];
+#pragma unroll
+    for (int j = 1; j < M; ++j) zmax = fmaxf(zmax, zv[e * M + j]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const float a = expf(zv[e * M + j] - zmax);
+      den += a;
+      num = fmaf(a, tot[e * M + j], num);
+    }
+    float kv = num / den;
+    const int ent = (t0 + e * M) / M;
+    if (rope_dim > 0 && c0 + kFewCh > d - rope_dim) {  // workgroup-uniform
+      const float other = __shfl_xor(kv, 1);
+      if (c >= d - rope_dim) {
+        const int i = (c - (d - rope_dim)) >> 1;
+        const double pos = (double)(pos0 + (long long)(ent % n_per_seq + 1) * M - 1);
+        double sn, cs;
+        sincos(pos * pow(theta, -2.0 * i / rope_dim), &sn, &cs);
+        const double u = (c & 1) ? other : kv, v = (c & 1) ? kv : other;
+        kv = (float)((c & 1) ? u * sn + v * cs : u * cs - v * sn);
+      }
+    }
+    if (is_c && t0 + e * M < n_tok) out[(size_t)ent * d + c] = kv;
+  }
+}
+
 bool compress_mfma_ok(bool bf16_in, int d_model, int d, int d_z) {
   return bf16_in && d_z == d && d % kMC == 0 && d_model % kMK == 0;
 }
@@ -273,6 +390,19 @@ hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_mode
                            double rope_theta, float* kv_out, hipStream_t st) {
   const int n_ent = T / m;
   if (B == 0 || n_ent == 0) return hipSuccess;
+  if (compress_mfma_ok(bf16_in, d_model, d, d_z) && (long long)B * T <= kFewTok && T % m == 0 &&
+      d_model % 128 == 0 && d % kFewCh == 0) {
+    const int nt = B * T;
+#define CSA2_FEW(M_)                                                                                  \
+  hipLaunchKernelGGL((compress_few_kernel<M_>), dim3(d / kFewCh), dim3(256), 0, st,                   \
+                     static_cast<const uint16_t*>(H), nt, d_model, static_cast<const uint16_t*>(W_kv), \
+                     static_cast<const uint16_t*>(W_z), d, pos0, rope_dim, rope_theta, n_ent, kv_out)
+    if (m == 1) CSA2_FEW(1);
+    else if (m == 2) CSA2_FEW(2);
+    else CSA2_FEW(4);
+#undef CSA2_FEW
+    return hipGetLastError();
+  }
   if (compress_mfma_ok(bf16_in, d_model, d, d_z)) {
     // Sequences shorter than a token tile whose tokens all fold (a decode step's
     // new block per sequence) are laid end to end as one run of B*T tokens: the

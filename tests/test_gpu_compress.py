@@ -28,6 +28,11 @@ def bd():
     (1, 1030, 320, 512, 512, 2, 24576, 64, True),
     (1, 200, 128, 128, 1, 2, 0, 64, True),
     (1, 64, 64, 64, 64, 1, 3, 0, True),
+    # a few tokens in all (a decode step's new blocks): the split-reduction kernel
+    (3, 2, 256, 512, 512, 2, 24576, 64, True),
+    (64, 1, 512, 512, 512, 1, 1000, 64, True),
+    (5, 4, 384, 256, 256, 4, 0, 64, True),
+    (2, 16, 128, 128, 128, 1, 7, 0, True),
 ])
 def test_compress(B, T, dm, d, dz, m, pos0, r, bf16):
     rng = np.random.default_rng(T + d)
