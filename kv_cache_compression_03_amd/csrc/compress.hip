@@ -268,10 +268,11 @@ __global__ __launch_bounds__(256, 1) void compress_mfma_kernel(
 // (B sequences of T tokens laid end to end).  The prefill kernel gives each
 // workgroup the whole 5,120-deep reduction for 64 channels, which at 64 tokens
 // leaves the GPU nearly idle.  Here a workgroup owns 8 channels (16 MFMA
-// columns: 8 of C, 8 of Z) for every token, and its four waves split the
-// reduction: wave w sums dims [w*d_model/4, (w+1)*d_model/4) into a partial
-// [64 tokens x 16 columns] tile, the four tiles are added through LDS in a fixed
-// order, and the fold and RoPE run as in the prefill kernel (a lane holds 4
+// columns: 8 of C, 8 of Z) for every token, and its NW waves (16 when d_model
+// allows, else 4) split the reduction: wave w sums dims
+// [w*d_model/NW, (w+1)*d_model/NW) into a partial [64 tokens x 16 columns]
+// tile, the tiles are added through LDS in wave order, and the first four waves
+// run the fold and RoPE as in the prefill kernel (a lane holds 4
 // consecutive tokens of one column; Z of the same channel is 8 lanes away).
 // Per 32-deep step a wave loads its 16 weight columns (16 B per lane: 8 channels
 // of W_KV or of W_Z of one reduction row), transposes them through a private LDS
@@ -281,16 +282,21 @@ constexpr int kFewTok = 64;   // tokens per workgroup
 constexpr int kFewCh = 8;     // channels per workgroup
 constexpr int kFewTP = 40;    // LDS pitch (bf16) of a transposed weight column
 
-template <int M>
-__global__ __launch_bounds__(256) void compress_few_kernel(
+template <int M, int NW>
+__global__ __launch_bounds__(64 * NW) void compress_few_kernel(
     const uint16_t* __restrict__ H, int n_tok, int d_model, const uint16_t* __restrict__ Wkv,
     const uint16_t* __restrict__ Wz, int d, long long pos0, int rope_dim, double theta,
     int n_per_seq, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[4][16 * kFewTP];  // per wave: [column][k]
-  __shared__ __attribute__((aligned(16))) float part[4][4 * 64 * 4];     // per wave: 4 tiles x 64 lanes x 4
+  __shared__ __attribute__((aligned(16))) uint16_t wt[NW][16 * kFewTP];  // per wave: [column][k]
+  __shared__ __attribute__((aligned(16))) float part[NW][4 * 64 * 4];     // per wave: 4 tiles x 64 lanes x 4
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
-  const int c0 = blockIdx.x * kFewCh;
-  const int kq = d_model / 4, k_lo = wave * kq;
+  // Workgroups go to the 8 XCDs round-robin by id.  Consecutive channel groups
+  // are placed on one XCD (when their count is a multiple of 8), so each
+  // 128-byte line of weights is fetched into one XCD's L2, not into all eight.
+  const int n_cg = gridDim.x;
+  const int cg = (n_cg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_cg >> 3) + (int)(blockIdx.x >> 3);
+  const int c0 = cg * kFewCh;
+  const int kq = d_model / NW, k_lo = wave * kq;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   // weight loads: lane l = reduction row l/2 of the step, W_KV (l even) or W_Z (odd)
   const uint16_t* wsrc = ((lane & 1) ? Wz : Wkv) + (size_t)(k_lo + (lane >> 1)) * d + c0;
@@ -331,18 +337,21 @@ __global__ __launch_bounds__(256) void compress_few_kernel(
       for (int rt = 0; rt < 4; ++rt) ha[rt] = ha_n[rt];
     }
   }
-  // ---- the four partial tiles, added in wave order
+  // ---- the NW partial tiles, added in wave order
   float4* mine = reinterpret_cast<float4*>(part[wave]);
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) mine[rt * 64 + lane] = make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]);
   __syncthreads();
+  if (wave >= 4) return;
   // wave w finishes token tile rt = w: lane holds tokens 16w + 4g + i of column col
-  f32x4_t tot;
+  f32x4_t tot = f32x4_t{0.f, 0.f, 0.f, 0.f};
   {
     const float4* p0 = reinterpret_cast<const float4*>(part[0]) + wave * 64 + lane;
-    const float4 a0 = p0[0], a1 = p0[256], a2 = p0[512], a3 = p0[768];
-    tot = f32x4_t{(a0.x + a1.x) + (a2.x + a3.x), (a0.y + a1.y) + (a2.y + a3.y),
-                  (a0.z + a1.z) + (a2.z + a3.z), (a0.w + a1.w) + (a2.w + a3.w)};
+    float4 a[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) a[w] = p0[w * 256];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += f32x4_t{a[w].x, a[w].y, a[w].z, a[w].w};
   }
   // columns 0-7 hold C, 8-15 Z of channels c0 .. c0+7: the Z of this lane's
   // channel is 8 lanes away
@@ -393,13 +402,19 @@ hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_mode
   if (compress_mfma_ok(bf16_in, d_model, d, d_z) && (long long)B * T <= kFewTok && T % m == 0 &&
       d_model % 128 == 0 && d % kFewCh == 0) {
     const int nt = B * T;
-#define CSA2_FEW(M_)                                                                                  \
-  hipLaunchKernelGGL((compress_few_kernel<M_>), dim3(d / kFewCh), dim3(256), 0, st,                   \
+#define CSA2_FEW(M_, NW_)                                                                             \
+  hipLaunchKernelGGL((compress_few_kernel<M_, NW_>), dim3(d / kFewCh), dim3(64 * NW_), 0, st,         \
                      static_cast<const uint16_t*>(H), nt, d_model, static_cast<const uint16_t*>(W_kv), \
                      static_cast<const uint16_t*>(W_z), d, pos0, rope_dim, rope_theta, n_ent, kv_out)
-    if (m == 1) CSA2_FEW(1);
-    else if (m == 2) CSA2_FEW(2);
-    else CSA2_FEW(4);
+    if (d_model % (32 * 16) == 0) {
+      if (m == 1) CSA2_FEW(1, 16);
+      else if (m == 2) CSA2_FEW(2, 16);
+      else CSA2_FEW(4, 16);
+    } else {
+      if (m == 1) CSA2_FEW(1, 4);
+      else if (m == 2) CSA2_FEW(2, 4);
+      else CSA2_FEW(4, 4);
+    }
 #undef CSA2_FEW
     return hipGetLastError();
   }

@@ -132,10 +132,90 @@ __global__ __launch_bounds__(256) void indexer_k_kernel(const uint8_t* __restric
   }
 }
 
+// A few hundred entries at most (a decode step's new entries): the kernel above
+// would give each of a handful of workgroups the whole projection and one long
+// chain of dependent float64 FMAs per thread.  Here a workgroup takes 32 key
+// columns of 2 entries and its four waves split the reduction: wave w stages rows
+// [w d/4, (w+1) d/4) of its [d x 32] slice of W in LDS (every load in flight at
+// once) and sums them in four interleaved float64 chains; the quarters are added
+// in wave order and the key is rounded to bf16 once.  Each product of a bf16
+// weight and a dequantised FP4 value has at most 14 significant bits, so the
+// float64 sum does not depend on its order unless its terms span more than
+// about 39 binades.
+constexpr int kIkCols = 32, kIkFew = 2;
+__global__ __launch_bounds__(256) void indexer_k_few_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            long long n, int d, long long cap,
+                                                            long long row, const uint16_t* __restrict__ W,
+                                                            int DI, uint16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) float xsf[];  // [kIkFew][d], [d][kIkCols] bf16, [4][64] f64
+  uint16_t* ws = reinterpret_cast<uint16_t*>(xsf + kIkFew * d);
+  double* qs = reinterpret_cast<double*>(ws + d * kIkCols);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long e0 = (long long)blockIdx.x * kIkFew;
+  const int c0 = blockIdx.y * kIkCols;
+  const int kq = d / 4, k_lo = wave * kq;
+  // this wave's rows of the W slice: a row is 64 bytes = 4 x 16 B, kq rows are
+  // kq / 16 loads per lane (at most 8: d <= 512)
+  {
+    uint4 buf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = i * 64 + lane;
+      if (t < kq * 4) buf[i] = *reinterpret_cast<const uint4*>(W + (size_t)(k_lo + (t >> 2)) * DI + c0 + 8 * (t & 3));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = i * 64 + lane;
+      if (t < kq * 4) reinterpret_cast<uint4*>(ws)[k_lo * 4 + t] = buf[i];
+    }
+  }
+  const int slabs = d / 8;
+  for (int t = tid; t < kIkFew * slabs; t += 256) {
+    const int el = t / slabs, sl = t - el * slabs;
+    const long long e = e0 + el, r = e * cap + row;
+    float v[8];
+    if (e < n) {
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + r * (d / 2) + sl * 4);
+      const float sc = e4m3_decode(scales[r * (d / 16) + (sl >> 1)]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((cw >> (4 * j)) & 15u) * sc;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xsf[el * d + sl * 8 + j] = v[j];
+  }
+  __syncthreads();
+  const int el = lane / kIkCols, cc = lane % kIkCols;
+  const float* xr = xsf + el * d;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+  for (int k = k_lo; k < k_lo + kq; k += 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = fma((double)xr[k + j], (double)bf16_to_f32(ws[(k + j) * kIkCols + cc]), acc[j]);
+  }
+  qs[wave * 64 + lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (wave != 0) return;
+  const double sum = (qs[lane] + qs[64 + lane]) + (qs[128 + lane] + qs[192 + lane]);
+  const long long e = e0 + el;
+  if (e < n) out[(e * cap + row) * DI + c0 + cc] = (uint16_t)f64_to_bf16_rne(sum);
+}
+
 hipError_t launch_indexer_k(const uint8_t* codes, const uint8_t* scales, long long n, int d,
                             const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st,
                             long long cap, long long row) {
   if (n == 0) return hipSuccess;
+  if (n <= 256 && d <= 512 && (reinterpret_cast<uintptr_t>(W_ik) & 15) == 0) {
+    const size_t lds = (size_t)kIkFew * d * sizeof(float) + (size_t)d * kIkCols * sizeof(uint16_t) +
+                       4 * 64 * sizeof(double);
+    hipLaunchKernelGGL(indexer_k_few_kernel, dim3((unsigned)((n + kIkFew - 1) / kIkFew), (unsigned)(d_i / kIkCols)),
+                       dim3(256), lds, st, codes, scales, n, d, cap, row, W_ik, d_i, k_idx);
+    return hipGetLastError();
+  }
   const int E = n >= 1024 ? 16 : 4;
   long long blocks = (n + E - 1) / E;
   size_t lds = (size_t)E * d * sizeof(float);

@@ -44,7 +44,8 @@ def test_quant_fp4_bit_exact(n, d):
     assert np.array_equal(codes.cpu().numpy(), ref.codes)
 
 
-@pytest.mark.parametrize("n,d,d_i", [(50, 256, 64), (1025, 512, 128)])
+@pytest.mark.parametrize("n,d,d_i", [(50, 256, 64), (1025, 512, 128), (64, 512, 128), (257, 512, 64),
+                                     (256, 512, 128), (1, 32, 64), (13, 96, 128)])
 def test_indexer_key_bit_exact(n, d, d_i):
     from kv_cache_compression_03_amd import binding as bd
     rng = np.random.default_rng(n)
