@@ -96,7 +96,8 @@ def algorithmic_bytes(wl) -> dict:
     its selected FP4 entries, its window, its query and writes its output."""
     entry = wl.d // 2 + wl.d // 16          # FP4 codes + E4M3 scales
     ik = wl.d_i * 2
-    per_attn = wl.K * entry + wl.S * wl.d + wl.H_q * wl.d * 2 + wl.H_q * wl.d * 4
+    # per query its selected entries, query and output; the window once per sequence
+    per_attn = wl.Tq * (wl.K * entry + wl.H_q * wl.d * 2 + wl.H_q * wl.d * 4) + wl.S * wl.d
     layers = wl.layers
     full = layers.count("F") * wl.B * wl.N * ik
     reidx = layers.count("R") * wl.B * wl.PB * wl.PE * ik
@@ -124,12 +125,12 @@ def build_inputs(wl, torch, bd, sch):
     log(f"cache built: {B} x {N} entries in {time.time() - t0:.1f}s")
     layers = []
     for li, mode in enumerate(wl.layers):
-        qm = np.stack([synth.q_main(wl, li, b) for b in range(B)])
+        qm = np.stack([synth.q_main(wl, li, b, wl.Tq) for b in range(B)])
         sw = np.stack([synth.swa_tokens(wl, li, b) for b in range(B)])
         qi = w = None
         if mode in "FR":
-            qi = np.stack([synth.q_index(wl, li, b) for b in range(B)])
-            w = np.stack([synth.head_weights(wl, li, b) for b in range(B)])
+            qi = np.stack([synth.q_index(wl, li, b, wl.Tq) for b in range(B)])
+            w = np.stack([synth.head_weights(wl, li, b, wl.Tq) for b in range(B)])
         tb = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         layers.append(sch.LayerBuffers(tb(qm), tt(sw), None if qi is None else tb(qi),
@@ -141,7 +142,7 @@ def time_scan(wl, torch, bd, kidx, layers, reps):
     """Average duration of the indexer-scan kernel launch (the dominant kernel),
     measured with HIP events on the stream it is launched on."""
     st = torch.cuda.current_stream()
-    scores = torch.empty(wl.B, 1, wl.N, dtype=torch.float32, device="cuda")
+    scores = torch.empty(wl.B, wl.Tq, wl.N, dtype=torch.float32, device="cuda")
     lb = layers[0]
     for _ in range(3):
         bd.csa2_index_full(lb.q_idx, lb.w, kidx, scores=scores)
@@ -165,27 +166,33 @@ def cpu_baseline(wl, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    from oracle.csa2 import swa_window_rows
     W = synth.w_ik(wl)
+    P, S = wl.N * wl.m, wl.S
     seqs = []
     for b in range(2):
         q8 = quant_fp4(synth.main_kv(wl, b))
         k = indexer_k(q8.codes, q8.scales, W)
-        lays = []
-        for li, mode in enumerate(wl.layers):
-            lays.append(LayerInputs(synth.q_main(wl, li, b)[0], synth.swa_tokens(wl, li, b),
-                                    synth.q_index(wl, li, b)[0] if mode in "FR" else None,
-                                    synth.head_weights(wl, li, b)[0] if mode in "FR" else None))
-        seqs.append((q8, k, lays))
+        for t in range(wl.Tq):   # query t sees the window tokens up to its own position
+            rows = (np.arange(S) if wl.Tq == 1 else
+                    swa_window_rows(P + t, S, P + wl.Tq - S, S - wl.Tq + 1))
+            lays = []
+            for li, mode in enumerate(wl.layers):
+                lays.append(LayerInputs(synth.q_main(wl, li, b, wl.Tq)[t],
+                                        synth.swa_tokens(wl, li, b)[rows],
+                                        synth.q_index(wl, li, b, wl.Tq)[t] if mode in "FR" else None,
+                                        synth.head_weights(wl, li, b, wl.Tq)[t] if mode in "FR" else None))
+            seqs.append((q8, k, lays))
     n, t0 = 0, time.perf_counter()
     while True:
-        q8, k, lays = seqs[n % 2]
+        q8, k, lays = seqs[n % len(seqs)]
         decode_step(wl.layers, lays, q8.codes, q8.scales, k, K=wl.K, G=wl.G, PB=wl.PB, PE=wl.PE)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
     return {"value": n / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} decode steps of sequences 0-1 of {wl.name} "
+            "sample": f"{n} single-query decode steps of sequences 0-1 of {wl.name} "
                       f"({'+'.join(wl.layers)}, {wl.N} entries), {el:.1f}s, float64 numpy"}
 
 
@@ -424,11 +431,16 @@ def main():
     codes, scales, kidx, layers = build_inputs(wl, torch, bd, sch)
     copy_calibration(args, torch)
     run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
-                             G=wl.G, PB=wl.PB, PE=wl.PE)
+                             G=wl.G, PB=wl.PB, PE=wl.PE, Tq=wl.Tq)
+    step_kw = {}
+    if wl.Tq > 1:   # the queries sit at positions P .. P+Tq-1; the window ends at the last
+        P = wl.N * wl.m
+        q_pos = (P + torch.arange(wl.Tq, dtype=torch.int32, device="cuda")).repeat(wl.B, 1)
+        step_kw = dict(q_pos=q_pos, swa_pos0=P + wl.Tq - wl.S, n_win=wl.S - wl.Tq + 1)
     if args.no_graph:
-        step = lambda: run.step(codes, scales, kidx, layers)
+        step = lambda: run.step(codes, scales, kidx, layers, **step_kw)
     else:
-        g = run.capture(codes, scales, kidx, layers)
+        g = run.capture(codes, scales, kidx, layers, **step_kw)
         step = g.replay
     for _ in range(args.warmup):
         step()
@@ -456,7 +468,7 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": wl.B / step_s,
+        "value": wl.B * wl.Tq / step_s,
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -469,7 +481,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "sequences": wl.B, "context_entries": wl.N, "m": wl.m,
                    "d": wl.d, "indexer": f"{wl.h_i}x{wl.d_i}", "heads": wl.H_q, "window": wl.S,
-                   "top_k": wl.K, "schedule": wl.schedule,
+                   "top_k": wl.K, "schedule": wl.schedule, "queries_per_sequence": wl.Tq,
                    "graph": not args.no_graph, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "index_scores_kernel (Full-layer indexer scan)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -28,7 +28,9 @@ constexpr int kScanWaves = 4;
 #endif
 constexpr int kScanBatch = CSA2_SCAN_BATCH;  // entry tiles whose keys are in flight together
 
-template <int HI, int DI>
+// QG query tiles per wave (several queries per sequence, e.g. drafted positions):
+// each key tile is loaded once and multiplied by all of them.
+template <int HI, int DI, int QG>
 __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, const int* __restrict__ gather,
@@ -39,32 +41,41 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int b = blockIdx.z;
-  const int t0 = blockIdx.y * QPT;
+  const int tw0 = blockIdx.y * QG * QPT;   // first query of this workgroup
 
-  // ---- queries (A operand) and head weights, kept for the whole range
-  bf16x8_t qa[KS];
-  {
-    const int t = t0 + col / HI, h = col % HI;
-    const uint4* qrow = reinterpret_cast<const uint4*>(q_idx + (((size_t)b * Tq + t) * HI + h) * DI);
+  // ---- queries (A operands) and head weights, kept for the whole range
+  bf16x8_t qa[QG][KS];
+  float wr[QG][4];
+  int nvis_row[QG];   // entries visible to this lane's query (decode: all)
+  bool writer[QG];
+  float* srow[QG];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < Tq) v = qrow[s * 4 + g];
-      qa[s] = as_bf16x8(v);
+  for (int qg = 0; qg < QG; ++qg) {
+    const int t0 = tw0 + qg * QPT;
+    {
+      const int t = t0 + col / HI, h = col % HI;
+      const uint4* qrow = reinterpret_cast<const uint4*>(q_idx + (((size_t)b * Tq + t) * HI + h) * DI);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < Tq) v = qrow[s * 4 + g];
+        qa[qg][s] = as_bf16x8(v);
+      }
     }
-  }
-  float wr[4];
-  int nvis_row = L;  // entries visible to this lane's query (decode: all)
-  const int myq = t0 + (4 * g) / HI;
+    const int myq = t0 + (4 * g) / HI;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i, t = t0 + r / HI;
-    wr[i] = t < Tq ? w[((size_t)b * Tq + t) * HI + (r % HI)] : 0.0f;
-  }
-  if (q_pos != nullptr && myq < Tq) {
-    long long p = q_pos[(size_t)b * Tq + myq];
-    long long nv = (p + 1) / m;
-    nvis_row = (int)(nv < 0 ? 0 : (nv > L ? L : nv));
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i, t = t0 + r / HI;
+      wr[qg][i] = t < Tq ? w[((size_t)b * Tq + t) * HI + (r % HI)] : 0.0f;
+    }
+    nvis_row[qg] = L;
+    if (q_pos != nullptr && myq < Tq) {
+      long long p = q_pos[(size_t)b * Tq + myq];
+      long long nv = (p + 1) / m;
+      nvis_row[qg] = (int)(nv < 0 ? 0 : (nv > L ? L : nv));
+    }
+    writer[qg] = (g % (HI / 4 >= 1 ? HI / 4 : 1)) == 0 && myq < Tq;
+    srow[qg] = scores + ((size_t)b * Tq + (myq < Tq ? myq : 0)) * L;
   }
   int Lb = L;
   if (gather_len != nullptr) Lb = min(L, gather_len[b]);
@@ -72,8 +83,6 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
   const long long wave_first = ((long long)blockIdx.x * kScanWaves + wave) * tiles_per_wave * 16;
   const uint16_t* kb = k_idx + (size_t)b * N * DI;
   const int* gb = gather ? gather + (size_t)b * L : nullptr;
-  const bool writer = (g % (HI / 4 >= 1 ? HI / 4 : 1)) == 0 && myq < Tq;
-  float* srow = scores + ((size_t)b * Tq + (myq < Tq ? myq : 0)) * L;
 
   for (int tile = 0; tile < tiles_per_wave; tile += kScanBatch) {
     uint4 kv[kScanBatch][KS];
@@ -101,16 +110,19 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) {
       if (tile + u >= tiles_per_wave) break;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mfma16x16x32(qa[s], as_bf16x8(kv[u][s]), acc);
-      float v = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v = fmaf(wr[i], fmaxf(acc[i], 0.0f), v);
-      if (HI >= 8) v += __shfl_xor(v, 16);
-      if (HI >= 16) v += __shfl_xor(v, 32);
       const int e = ent[u];
-      if (writer && e < L) srow[e] = (ent_ok[u] && e < nvis_row) ? v : -INFINITY;
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma16x16x32(qa[qg][s], as_bf16x8(kv[u][s]), acc);
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wr[qg][i], fmaxf(acc[i], 0.0f), v);
+        if (HI >= 8) v += __shfl_xor(v, 16);
+        if (HI >= 16) v += __shfl_xor(v, 32);
+        if (writer[qg] && e < L) srow[qg][e] = (ent_ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
+      }
     }
   }
 }
@@ -123,7 +135,10 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   if (L == N && index_prefill_supported(Tq, N, h_i, d_i, gather))
     return launch_index_prefill(q_idx, w, k_idx, q_pos, m, B, Tq, N, h_i, d_i, scores, st);
   const int qpt = 16 / h_i;
-  const int qgroups = (Tq + qpt - 1) / qpt;
+  const int qtiles = (Tq + qpt - 1) / qpt;
+  // query tiles per wave: every key tile is read once for up to four of them
+  const int qg = qtiles >= 4 ? 4 : qtiles;
+  const int qgroups = (qtiles + qg - 1) / qg;
   const long long tiles = ((long long)L + 15) / 16;
   // aim for about CSA2_SCAN_TARGET_WGS workgroups, at most 32 tiles (512 entries) per wave
   const long long target = CSA2_SCAN_TARGET_WGS;
@@ -132,9 +147,16 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   tpw = (tpw + kScanBatch - 1) / kScanBatch * kScanBatch;
   const long long bx = (tiles + (long long)tpw * kScanWaves - 1) / ((long long)tpw * kScanWaves);
   dim3 grid((unsigned)bx, (unsigned)qgroups, (unsigned)B), block(kScanWaves * 64);
-#define CSA2_SCAN(HI_, DI_)                                                                    \
-  hipLaunchKernelGGL((index_scores_kernel<HI_, DI_>), grid, block, 0, st, q_idx, w, k_idx, gather, \
+#define CSA2_SCAN_Q(HI_, DI_, QG_)                                                                   \
+  hipLaunchKernelGGL((index_scores_kernel<HI_, DI_, QG_>), grid, block, 0, st, q_idx, w, k_idx, gather, \
                      gather_len, q_pos, m, Tq, N, L, tpw, scores)
+#define CSA2_SCAN(HI_, DI_)                     \
+  do {                                          \
+    if (qg == 1) CSA2_SCAN_Q(HI_, DI_, 1);      \
+    else if (qg == 2) CSA2_SCAN_Q(HI_, DI_, 2); \
+    else if (qg == 3) CSA2_SCAN_Q(HI_, DI_, 3); \
+    else CSA2_SCAN_Q(HI_, DI_, 4);              \
+  } while (0)
   if (h_i == 8 && d_i == 128) CSA2_SCAN(8, 128);
   else if (h_i == 8 && d_i == 64) CSA2_SCAN(8, 64);
   else if (h_i == 4 && d_i == 128) CSA2_SCAN(4, 128);
@@ -142,6 +164,7 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   else if (h_i == 16 && d_i == 128) CSA2_SCAN(16, 128);
   else CSA2_SCAN(16, 64);
 #undef CSA2_SCAN
+#undef CSA2_SCAN_Q
   return hipGetLastError();
 }
 

@@ -38,8 +38,15 @@ class LayerBuffers:
 class DecodeSchedule:
     def __init__(self, schedule: Sequence[str], B: int, N: int, d: int, h_i: int, d_i: int,
                  H_q: int, S: int, K: int = 512, G: int = 128, PB: int = 2048, PE: int = 8,
-                 swa_scale: float = 1.0, device: str = "cuda"):
+                 swa_scale: float = 1.0, device: str = "cuda", Tq: int = 1):
+        """Tq > 1: several queries per sequence in one step (a token and the positions
+        drafted after it), each with its own Top-K from one shared scan of the keys.
+        Reindex rescoring takes one query per sequence, so it needs Tq = 1."""
         self.layers: List[str] = list(schedule)
+        if Tq < 1:
+            raise ValueError("Tq must be >= 1")
+        if Tq > 1 and REINDEX in self.layers:
+            raise ValueError("Reindex layers take one query per sequence (Tq = 1)")
         for i, mode in enumerate(self.layers):
             if mode not in (FULL, REINDEX, REUSE, SWA_ONLY):
                 raise ValueError(f"layer {i}: unknown mode {mode!r}")
@@ -47,23 +54,23 @@ class DecodeSchedule:
                 raise ValueError(f"layer {i}: Reuse before any Full/Reindex layer")
             if mode == REINDEX and FULL not in self.layers[:i]:
                 raise ValueError(f"layer {i}: Reindex before any Full layer")
-        self.B, self.N, self.d, self.h_i, self.d_i = B, N, d, h_i, d_i
+        self.B, self.Tq, self.N, self.d, self.h_i, self.d_i = B, Tq, N, d, h_i, d_i
         self.H_q, self.S, self.K, self.G, self.PB, self.PE = H_q, S, K, G, PB, PE
         self.swa_scale = swa_scale
         self.need_pool = REINDEX in self.layers
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
-        self.scores = torch.empty(B, 1, N, dtype=torch.float32, device=dev)
-        self.sel: Dict[int, torch.Tensor] = {i: torch.empty(B, 1, K, **i32)
+        self.scores = torch.empty(B, Tq, N, dtype=torch.float32, device=dev)
+        self.sel: Dict[int, torch.Tensor] = {i: torch.empty(B, Tq, K, **i32)
                                              for i, m in enumerate(self.layers) if m in (FULL, REINDEX)}
-        self.no_sel = torch.full((B, 1, K), -1, **i32)
+        self.no_sel = torch.full((B, Tq, K), -1, **i32)
         self.pool = torch.empty(B, PB * PE, **i32) if self.need_pool else None
         self.pool_len = torch.empty(B, **i32) if self.need_pool else None
-        self.out = [torch.empty(B, 1, H_q, d, dtype=torch.float32, device=dev) for _ in self.layers]
-        ws = max(bd.csa2_index_full_workspace(B, 1, N, G, PB, PE) if self.need_pool else 0,
-                 bd.csa2_topk_workspace(B, N, K),
+        self.out = [torch.empty(B, Tq, H_q, d, dtype=torch.float32, device=dev) for _ in self.layers]
+        ws = max(bd.csa2_index_full_workspace(B, Tq, N, G, PB, PE) if self.need_pool else 0,
+                 bd.csa2_topk_workspace(B * Tq, N, K),
                  bd.csa2_index_reindex_workspace(B, PB * PE, K) if self.need_pool else 0,
-                 bd.csa2_sparse_attn_workspace(B, 1, H_q, d, K, S))
+                 bd.csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
 
     def selection_of(self, layer: int) -> torch.Tensor:
@@ -76,9 +83,12 @@ class DecodeSchedule:
         raise ValueError("no selection")
 
     def step(self, codes: torch.Tensor, scales: torch.Tensor, k_idx: torch.Tensor,
-             layers: Sequence[LayerBuffers], stream=None) -> List[torch.Tensor]:
-        """One decode query per sequence through every layer; returns the per-layer outputs."""
-        B, K = self.B, self.K
+             layers: Sequence[LayerBuffers], stream=None, q_pos=None, swa_pos0: int = 0,
+             n_win: int = 128) -> List[torch.Tensor]:
+        """Tq decode queries per sequence through every layer; returns the per-layer
+        outputs.  q_pos [B, Tq] (optional) limits each query's window to the tokens
+        at positions (t - n_win, t], window slot i holding position swa_pos0 + i."""
+        B, K, R = self.B, self.K, self.B * self.Tq
         pool_built = False
         for i, (mode, lb) in enumerate(zip(self.layers, layers)):
             if mode == FULL:
@@ -88,28 +98,28 @@ class DecodeSchedule:
                                    pool_len=self.pool_len if build else None,
                                    G=self.G, PB=self.PB, PE=self.PE, ws=self.ws, stream=stream)
                 pool_built = pool_built or build
-                bd.csa2_topk(self.scores.view(B, self.N), K, out=self.sel[i].view(B, K), ws=self.ws,
+                bd.csa2_topk(self.scores.view(R, self.N), K, out=self.sel[i].view(R, K), ws=self.ws,
                              stream=stream)
             elif mode == REINDEX:
                 bd.csa2_index_reindex(lb.q_idx.view(B, self.h_i, self.d_i), lb.w.view(B, self.h_i),
                                       k_idx, self.pool, self.pool_len, K,
                                       sel=self.sel[i].view(B, K), ws=self.ws, stream=stream)
             bd.csa2_sparse_attn(lb.q_main, codes, scales, self.selection_of(i), lb.swa,
-                                swa_scale=self.swa_scale, out=self.out[i], ws=self.ws,
-                                stream=stream)
+                                swa_scale=self.swa_scale, q_pos=q_pos, swa_pos0=swa_pos0,
+                                n_win=n_win, out=self.out[i], ws=self.ws, stream=stream)
         return self.out
 
-    def capture(self, codes, scales, k_idx, layers, warmup: int = 1) -> torch.cuda.CUDAGraph:
+    def capture(self, codes, scales, k_idx, layers, warmup: int = 1, **step_kw) -> torch.cuda.CUDAGraph:
         """Capture one step into a graph (after `warmup` eager steps on a side stream)."""
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for _ in range(warmup):
-                self.step(codes, scales, k_idx, layers)
+                self.step(codes, scales, k_idx, layers, **step_kw)
         torch.cuda.current_stream().wait_stream(s)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step(codes, scales, k_idx, layers)
+            self.step(codes, scales, k_idx, layers, **step_kw)
         return g
 
 

@@ -65,6 +65,10 @@ class Workload:
     # decode cache append: one new entry per sequence into row N-1 of an N-row
     # cache, and the token's window KV into every layer's window
     append: bool = False
+    # decode with Tq queries per sequence (a token and the positions drafted after
+    # it, the first at position N*m): one shared scan of the keys, a Top-K per
+    # query; the window buffer holds n_win + Tq - 1 tokens ending at the last one
+    Tq: int = 1
 
     @property
     def pos0(self) -> int:
@@ -108,6 +112,9 @@ WORKLOADS = {
     "prefill_32k": Workload("prefill_32k", B=1, N=16384, d=512, h_i=8, d_i=128, H_q=64,
                             S=8192 + 127, m=2, schedule="FUUUUU", seed=3, T=32768,
                             chunk=8192, d_model=5120, h_dtype="bf16"),
+    # decode_64k_b64 with 6 queries per sequence (1 + 5 drafted positions)
+    "mtp_64k_b64": Workload("mtp_64k_b64", B=64, N=65536, d=512, h_i=8, d_i=128, H_q=64,
+                            S=128 + 5, schedule="FUUU", seed=6, Tq=6),
     # decode cache append: 64 sequences, d = 512 entries with 128-dim keys, the
     # token's window KV for the 20 decoder layers (128-token windows); the entry
     # comes from hidden states of width 5,120 (bf16) through the compressor

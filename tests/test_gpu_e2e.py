@@ -6,7 +6,8 @@ import torch
 
 import synth
 from helpers import attn_close, check_topk, dev, dev_bf16, host_bf16_bits
-from oracle.csa2 import (LayerInputs, compress, decode_step, index_scores, indexer_k, quant_fp4)
+from oracle.csa2 import (LayerInputs, compress, decode_step, index_scores, indexer_k, quant_fp4,
+                         sparse_attention, topk)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +134,61 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(eager, run.out):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("Tq,sched", [(6, "FUUS"), (3, "FUFU")])
+def test_multi_query_decode(Tq, sched):
+    """Several queries per sequence in one step (a token and the positions drafted
+    after it): every query gets its own Full Top-K from one shared scan of the keys
+    and attends to its selection and to the window tokens up to its own position
+    (the window buffer holds n_win + Tq - 1 tokens ending at the last draft)."""
+    bd, sch = mods()
+    n_win = 128
+    S = n_win + Tq - 1
+    wl = synth.workload("decode_64k_b64", B=2, N=7000, schedule=sched, K=128, S=S)
+    B, P = wl.B, 50_000                          # the first query's position
+    kv = np.stack([synth.main_kv(wl, b) for b in range(B)])
+    Wik = synth.w_ik(wl)
+    codes, scales, kidx = bd.csa2_quant_fp4(dev(kv), W_ik=dev_bf16(Wik))
+    qm = [np.stack([synth.q_main(wl, li, b, Tq) for b in range(B)]) for li in range(len(sched))]
+    sw = [np.stack([synth.swa_tokens(wl, li, b, S=S) for b in range(B)]) for li in range(len(sched))]
+    qi = {li: np.stack([synth.q_index(wl, li, b, Tq) for b in range(B)]) for li, mo in enumerate(sched) if mo == "F"}
+    ww = {li: np.stack([synth.head_weights(wl, li, b, Tq) for b in range(B)]) for li in qi}
+    devl = [sch.LayerBuffers(q_main=dev_bf16(qm[li]), swa=dev(sw[li]),
+                             q_idx=dev_bf16(qi[li]) if li in qi else None,
+                             w=dev(ww[li]) if li in ww else None) for li in range(len(sched))]
+    q_pos = np.broadcast_to(P + np.arange(Tq, dtype=np.int32), (B, Tq)).copy()
+    swa_pos0 = P + Tq - S
+    run = sch.DecodeSchedule(wl.layers, B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, S, wl.K, Tq=Tq)
+    outs = [o.cpu().numpy() for o in run.step(codes, scales, kidx, devl, q_pos=dev(q_pos),
+                                               swa_pos0=swa_pos0, n_win=n_win)]
+    codes_h, scales_h = codes.cpu().numpy(), scales.cpu().numpy()
+    compared = skipped = 0
+    for b in range(B):
+        q8 = quant_fp4(kv[b])
+        k_ref = indexer_k(q8.codes, q8.scales, Wik)
+        last = None                                                # latest Full selections
+        for li, mode in enumerate(sched):
+            gsel = run.selection_of(li).cpu().numpy()[b]          # [Tq, K]
+            if mode == "F":
+                wants = []
+                for t in range(Tq):
+                    s = index_scores(qi[li][b, t], ww[li][b, t], k_ref)
+                    check_topk(gsel[t], s, wl.K)
+                    wants.append(topk(s, wl.K))
+                last = wants
+            elif mode == "U":
+                assert np.array_equal(gsel, run.selection_of(li - 1).cpu().numpy()[b])
+                wants = last
+            else:
+                assert np.all(gsel == -1)
+                wants = list(gsel)
+            for t in range(Tq):
+                if not np.array_equal(gsel[t], wants[t]):
+                    skipped += 1                                  # a near-tie changed the selection
+                    continue
+                ref = sparse_attention(qm[li][b, t], codes_h[b], scales_h[b], wants[t], sw[li][b],
+                                       q_pos=int(q_pos[b, t]), swa_pos0=swa_pos0, n_win=n_win)
+                attn_close(outs[li][b, t], ref)
+                compared += 1
+    assert skipped <= compared // 4

@@ -36,9 +36,19 @@ def test_scores_and_topk(B, N, h_i, d_i):
         check_topk(sel[b], ref, 512)
 
 
-def test_scores_with_positions():
-    B, Tq, N, h_i, d_i, m = 2, 5, 3000, 8, 128, 2
-    rng = np.random.default_rng(1)
+@pytest.mark.parametrize("Tq,h_i,d_i", [
+    (5, 8, 128),    # 3 query tiles, one workgroup row holds all three
+    (20, 8, 128),   # 10 query tiles: three workgroup rows of four, the last one partial
+    (3, 16, 64),    # one query per tile
+    (9, 4, 128),    # four queries per tile, the last tile partial
+    (2, 8, 64),     # one tile
+])
+def test_scores_with_positions(Tq, h_i, d_i):
+    """Several queries per sequence (drafted positions, prefill rows below the
+    prefill kernel's size) share one pass over the keys: every query's scores,
+    visibility and Top-K."""
+    B, N, m = 2, 3000, 2
+    rng = np.random.default_rng(1 + Tq)
     q = rand_bf16(rng, (B, Tq, h_i, d_i))
     w = rng.random((B, Tq, h_i)).astype(np.float32)
     k = rand_bf16(rng, (B, N, d_i))
