@@ -103,6 +103,22 @@ CSA2_API int csa2_quant_fp4(const float* kv, long long n, int d, uint8_t* codes,
                             const void* W_ik, int d_i, void* k_idx, void* stream);
 
 /*
+ * csa2_indexer_keys -- the indexer keys of an existing FP4 cache.
+ * [deep-dive §3.4] only the FP4 global KV is persisted; [deep-dive §3.1] the
+ * indexer K is a projection of the main KV.  Reading: the key is formed from the
+ * dequantised entry, so a cache reloaded from its codes and scales gets back
+ * bit-identical keys: k_idx = bf16(dequant(codes, scales) · W_ik), float64 sums,
+ * one rounding (the keys csa2_quant_fp4 writes).
+ *   codes  [n, d/2] u8, scales [n, d/16] u8 E4M3 (as csa2_quant_fp4 writes them)
+ *   W_ik   [d, d_i] bf16;  k_idx [n, d_i] bf16 (written)
+ * Device pointers, owned by the caller; enqueued on `stream`.  Errors
+ * (CSA2_ERR_INVALID_ARG / CSA2_ERR_UNSUPPORTED) are returned before any launch.
+ * Limits: d % 32 == 0 and d <= 512; d_i in {64, 128}.
+ */
+CSA2_API int csa2_indexer_keys(const uint8_t* codes, const uint8_t* scales, long long n, int d,
+                               const void* W_ik, int d_i, void* k_idx, void* stream);
+
+/*
  * csa2_cache_append -- decode-step cache append: one new Main-KV entry per
  * sequence into row `row` of each sequence's FP4 cache (with its indexer key),
  * and the new token's window KV into slot `slot` of each layer's window.

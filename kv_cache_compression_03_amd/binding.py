@@ -30,6 +30,7 @@ _SIGS = {
     "csa2_compress": ([_c_p, _c_i, _c_i, _c_i, _c_i, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_ll,
                        _c_i, _c_d, _c_p, _c_p], _c_i),
     "csa2_quant_fp4": ([_c_p, _c_ll, _c_i, _c_p, _c_p, _c_p, _c_i, _c_p, _c_p], _c_i),
+    "csa2_indexer_keys": ([_c_p, _c_p, _c_ll, _c_i, _c_p, _c_i, _c_p, _c_p], _c_i),
     "csa2_cache_append": ([_c_p, _c_i, _c_i, _c_ll, _c_ll, _c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_i,
                            _c_i, _c_i, _c_f, _c_p, _c_p], _c_i),
     "csa2_index_full_workspace": ([_c_i, _c_i, _c_i, _c_i, _c_i, _c_i], _c_sz),
@@ -184,6 +185,27 @@ def csa2_quant_fp4(kv, codes=None, scales=None, W_ik=None, k_idx=None, stream=No
     _call("csa2_quant_fp4", _p(kv), n, d, _p(codes), _p(scales), _p(W_ik), d_i, _p(k_idx),
           _stream(stream))
     return (codes, scales) if W_ik is None else (codes, scales, k_idx)
+
+
+def csa2_indexer_keys(codes, scales, W_ik, k_idx=None, stream=None) -> torch.Tensor:
+    """codes [..., d/2] u8, scales [..., d/16] u8, W_ik [d, d_i] bf16 -> k_idx [..., d_i] bf16
+    (the keys of an existing FP4 cache, e.g. one reloaded from its codes and scales)."""
+    _dev(codes, "codes", U8)
+    _dev(scales, "scales", U8)
+    _dev(W_ik, "W_ik", BF16)
+    d = codes.shape[-1] * 2
+    lead = codes.shape[:-1]
+    if tuple(scales.shape) != tuple(lead) + (d // 16,):
+        raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
+    if W_ik.shape[0] != d:
+        raise ValueError(f"W_ik has {W_ik.shape[0]} rows, entries have {d} channels")
+    n = codes.numel() // (d // 2)
+    d_i = W_ik.shape[1]
+    if k_idx is None:
+        k_idx = torch.empty(*lead, d_i, dtype=torch.bfloat16, device=codes.device)
+    _dev(k_idx, "k_idx", BF16)
+    _call("csa2_indexer_keys", _p(codes), _p(scales), n, d, _p(W_ik), d_i, _p(k_idx), _stream(stream))
+    return k_idx
 
 
 def csa2_cache_append(codes, scales, row: int, kv=None, W_ik=None, k_idx=None, win=None, swa=None,

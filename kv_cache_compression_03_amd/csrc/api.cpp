@@ -125,6 +125,22 @@ CSA2_API int csa2_quant_fp4(const float* kv, long long n, int d, uint8_t* codes,
   return hip_status(e, fn);
 }
 
+CSA2_API int csa2_indexer_keys(const uint8_t* codes, const uint8_t* scales, long long n, int d,
+                               const void* W_ik, int d_i, void* k_idx, void* stream) {
+  const char* fn = "csa2_indexer_keys";
+  CHECK(n >= 0, CSA2_ERR_INVALID_ARG, "%s: n < 0", fn);
+  CHECK(d > 0 && d % 32 == 0 && d <= 512, CSA2_ERR_UNSUPPORTED, "%s: d must be a multiple of 32 in [32, 512]", fn);
+  CHECK(d_i == 64 || d_i == 128, CSA2_ERR_UNSUPPORTED, "%s: d_i must be 64 or 128", fn);
+  if (n == 0) return ok();
+  NEED_PTR(codes);
+  NEED_PTR(scales);
+  NEED_PTR(W_ik);
+  NEED_PTR(k_idx);
+  return hip_status(csa2::launch_indexer_k(codes, scales, n, d, static_cast<const uint16_t*>(W_ik), d_i,
+                                           static_cast<uint16_t*>(k_idx), S(stream)),
+                    fn);
+}
+
 // ------------------------------------------------------------------ decode cache append
 
 CSA2_API int csa2_cache_append(const float* kv, int B, int d, long long cap, long long row,

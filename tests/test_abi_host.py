@@ -81,6 +81,12 @@ def test_invalid_arguments_rejected_before_launch():
     assert L.csa2_cache_append(None, 4, 512, 8, 0, p, p, None, 0, None, p, 2, 128, 3, 0.0, p, None) == 1
     assert L.csa2_cache_append(None, 4, 40, 8, 0, p, p, None, 0, None, None, 0, 0, 0, 1.0, None, None) == 2
     assert L.csa2_cache_append(p, 4, 512, 8, 0, p, p, p, 0, None, None, 0, 0, 0, 1.0, None, None) == 1
+    # keys of an existing cache: unsupported widths, missing buffers
+    assert L.csa2_indexer_keys(p, p, 16, 1024, p, 128, p, None) == 2
+    assert L.csa2_indexer_keys(p, p, 16, 512, p, 96, p, None) == 2
+    st = L.csa2_indexer_keys(p, p, 16, 512, None, 128, p, None)
+    assert st == 1 and b"W_ik is null" in L.csa2_last_error()
+    assert L.csa2_indexer_keys(None, None, 0, 512, None, 128, None, None) == 0
     # empty work is a no-op success
     assert L.csa2_quant_fp4(None, 0, 512, None, None, None, 0, None, None) == 0
     assert L.csa2_last_error() == b""
