@@ -182,6 +182,8 @@ def csa2_quant_fp4(kv, codes=None, scales=None, W_ik=None, k_idx=None, stream=No
         if k_idx is None:
             k_idx = torch.empty(*lead, d_i, dtype=torch.bfloat16, device=kv.device)
         _dev(k_idx, "k_idx", BF16)
+    if n == 0:   # nothing to quantise (an empty tensor has no data pointer to pass)
+        return (codes, scales) if W_ik is None else (codes, scales, k_idx)
     _call("csa2_quant_fp4", _p(kv), n, d, _p(codes), _p(scales), _p(W_ik), d_i, _p(k_idx),
           _stream(stream))
     return (codes, scales) if W_ik is None else (codes, scales, k_idx)

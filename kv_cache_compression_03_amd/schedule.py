@@ -38,15 +38,20 @@ class LayerBuffers:
 class DecodeSchedule:
     def __init__(self, schedule: Sequence[str], B: int, N: int, d: int, h_i: int, d_i: int,
                  H_q: int, S: int, K: int = 512, G: int = 128, PB: int = 2048, PE: int = 8,
-                 swa_scale: float = 1.0, device: str = "cuda", Tq: int = 1):
+                 swa_scale: float = 1.0, device: str = "cuda", Tq: int = 1,
+                 full_in_pool: bool = False):
         """Tq > 1: several queries per sequence in one step (a token and the positions
         drafted after it), each with its own Top-K from one shared scan of the keys.
-        Reindex rescoring takes one query per sequence, so it needs Tq = 1."""
+        Reindex rescoring takes one query per sequence, so it needs Tq = 1.
+        full_in_pool: a Full layer takes its Top-K inside the candidate pool built
+        from its own scores rather than over every entry (the other reading of the
+        Full layer's selection); one query per sequence."""
         self.layers: List[str] = list(schedule)
         if Tq < 1:
             raise ValueError("Tq must be >= 1")
-        if Tq > 1 and REINDEX in self.layers:
-            raise ValueError("Reindex layers take one query per sequence (Tq = 1)")
+        if Tq > 1 and (REINDEX in self.layers or full_in_pool):
+            raise ValueError("Reindex and pool-restricted Full layers take one query per sequence (Tq = 1)")
+        self.full_in_pool = full_in_pool
         for i, mode in enumerate(self.layers):
             if mode not in (FULL, REINDEX, REUSE, SWA_ONLY):
                 raise ValueError(f"layer {i}: unknown mode {mode!r}")
@@ -57,7 +62,7 @@ class DecodeSchedule:
         self.B, self.Tq, self.N, self.d, self.h_i, self.d_i = B, Tq, N, d, h_i, d_i
         self.H_q, self.S, self.K, self.G, self.PB, self.PE = H_q, S, K, G, PB, PE
         self.swa_scale = swa_scale
-        self.need_pool = REINDEX in self.layers
+        self.need_pool = REINDEX in self.layers or (full_in_pool and FULL in self.layers)
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         self.scores = torch.empty(B, Tq, N, dtype=torch.float32, device=dev)
@@ -92,14 +97,19 @@ class DecodeSchedule:
         pool_built = False
         for i, (mode, lb) in enumerate(zip(self.layers, layers)):
             if mode == FULL:
-                build = self.need_pool and not pool_built
+                build = (self.need_pool and not pool_built) or self.full_in_pool
                 bd.csa2_index_full(lb.q_idx, lb.w, k_idx, scores=self.scores,
                                    pool=self.pool if build else None,
                                    pool_len=self.pool_len if build else None,
                                    G=self.G, PB=self.PB, PE=self.PE, ws=self.ws, stream=stream)
                 pool_built = pool_built or build
-                bd.csa2_topk(self.scores.view(R, self.N), K, out=self.sel[i].view(R, K), ws=self.ws,
-                             stream=stream)
+                if self.full_in_pool:   # the Top-K inside the pool this layer just built
+                    bd.csa2_index_reindex(lb.q_idx.view(B, self.h_i, self.d_i), lb.w.view(B, self.h_i),
+                                          k_idx, self.pool, self.pool_len, K,
+                                          sel=self.sel[i].view(B, K), ws=self.ws, stream=stream)
+                else:
+                    bd.csa2_topk(self.scores.view(R, self.N), K, out=self.sel[i].view(R, K),
+                                 ws=self.ws, stream=stream)
             elif mode == REINDEX:
                 bd.csa2_index_reindex(lb.q_idx.view(B, self.h_i, self.d_i), lb.w.view(B, self.h_i),
                                       k_idx, self.pool, self.pool_len, K,

@@ -7,7 +7,7 @@ import torch
 import synth
 from helpers import attn_close, check_topk, dev, dev_bf16, host_bf16_bits
 from oracle.csa2 import (LayerInputs, compress, decode_step, index_scores, indexer_k, quant_fp4,
-                         sparse_attention, topk)
+                         build_pool, reindex, sparse_attention, topk)
 
 pytestmark = pytest.mark.gpu
 
@@ -192,3 +192,44 @@ def test_multi_query_decode(Tq, sched):
                 attn_close(outs[li][b, t], ref)
                 compared += 1
     assert skipped <= compared // 4
+
+
+def test_full_layer_top_k_inside_the_pool():
+    """The other reading of the Full layer's selection: its Top-K taken inside the
+    candidate pool built from its own scores.  Pool against the oracle's pool
+    (near-tie exemption), selection against the oracle's Top-K inside that pool,
+    Reuse of it, attention on identical selections."""
+    bd, sch = mods()
+    wl = synth.workload("reindex_256k_b32", B=3, N=20000, schedule="FUU", PB=64, PE=8, K=128,
+                        plant_frac=0.01)
+    B = wl.B
+    kv = np.stack([synth.main_kv(wl, b) for b in range(B)])
+    Wik = synth.w_ik(wl)
+    codes, scales, kidx = bd.csa2_quant_fp4(dev(kv), W_ik=dev_bf16(Wik))
+    host, devl = layer_inputs(wl, B, wl.layers)
+    run = sch.DecodeSchedule(wl.layers, B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
+                             G=wl.G, PB=wl.PB, PE=wl.PE, full_in_pool=True)
+    outs = [o.cpu().numpy() for o in run.step(codes, scales, kidx, devl)]
+    codes_h, scales_h, kidx_h = codes.cpu().numpy(), scales.cpu().numpy(), host_bf16_bits(kidx)
+    compared = 0
+    for b in range(B):
+        li_in = host[b][0]
+        s = index_scores(li_in.q_idx, li_in.w, kidx_h[b])
+        pool = build_pool(s, wl.G, wl.PB, wl.PE)
+        gpool = run.pool.cpu().numpy()[b, :run.pool_len[b].item()]
+        assert len(set(gpool.tolist()) ^ set(pool.tolist())) <= 2
+        gsel = run.selection_of(0).cpu().numpy()[b, 0]
+        assert set(gsel[gsel >= 0].tolist()) <= set(gpool.tolist())
+        if not np.array_equal(gpool, pool):
+            continue
+        check_topk(gsel, index_scores(li_in.q_idx, li_in.w, kidx_h[b][pool]), wl.K, index_map=pool)
+        want = reindex(li_in.q_idx, li_in.w, kidx_h[b], pool, wl.K)
+        for li in (1, 2):
+            assert np.array_equal(run.selection_of(li).cpu().numpy()[b, 0], gsel)
+        if np.array_equal(gsel, want):
+            for li in range(len(wl.layers)):
+                ref = sparse_attention(host[b][li].q_main, codes_h[b], scales_h[b], want,
+                                       host[b][li].swa)
+                attn_close(outs[li][b, 0], ref)
+            compared += 1
+    assert compared >= 2
