@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--full-in-pool", action="store_true",
+                    help="decode: Full layers take their Top-K inside the candidate pool built from "
+                         "their own scores (the other reading of the Full selection)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size reference "
                          "for HBM byte counters)")
@@ -431,7 +434,7 @@ def main():
     codes, scales, kidx, layers = build_inputs(wl, torch, bd, sch)
     copy_calibration(args, torch)
     run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
-                             G=wl.G, PB=wl.PB, PE=wl.PE, Tq=wl.Tq)
+                             G=wl.G, PB=wl.PB, PE=wl.PE, Tq=wl.Tq, full_in_pool=args.full_in_pool)
     step_kw = {}
     if wl.Tq > 1:   # the queries sit at positions P .. P+Tq-1; the window ends at the last
         P = wl.N * wl.m
@@ -482,6 +485,7 @@ def main():
         "config": {"workload": wl.name, "sequences": wl.B, "context_entries": wl.N, "m": wl.m,
                    "d": wl.d, "indexer": f"{wl.h_i}x{wl.d_i}", "heads": wl.H_q, "window": wl.S,
                    "top_k": wl.K, "schedule": wl.schedule, "queries_per_sequence": wl.Tq,
+                   "full_top_k": "inside the pool" if args.full_in_pool else "global",
                    "graph": not args.no_graph, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "index_scores_kernel (Full-layer indexer scan)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
