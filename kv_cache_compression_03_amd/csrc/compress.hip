@@ -268,17 +268,20 @@ __global__ __launch_bounds__(256, 1) void compress_mfma_kernel(
 // (B sequences of T tokens laid end to end).  The prefill kernel gives each
 // workgroup the whole 5,120-deep reduction for 64 channels, which at 64 tokens
 // leaves the GPU nearly idle.  Here a workgroup owns 8 channels (16 MFMA
-// columns: 8 of C, 8 of Z) for every token, and its NW waves (16 when d_model
-// allows, else 4) split the reduction: wave w sums dims
-// [w*d_model/NW, (w+1)*d_model/NW) into a partial [64 tokens x 16 columns]
-// tile, the tiles are added through LDS in wave order, and the first four waves
-// run the fold and RoPE as in the prefill kernel (a lane holds 4
-// consecutive tokens of one column; Z of the same channel is 8 lanes away).
+// columns: 8 of C, 8 of Z) of one 16-token tile, and its NW waves (16 when
+// d_model allows, else 4) split the reduction: wave w sums dims
+// [w*d_model/NW, (w+1)*d_model/NW) into a partial [16 tokens x 16 columns]
+// tile, the tiles are added through LDS in wave order, and the first wave runs
+// the fold and RoPE as in the prefill kernel (a lane holds 4 consecutive tokens
+// of one column; Z of the same channel is 8 lanes away).  A workgroup moves its
+// tile's hidden states and its channels' weight columns: one tile per
+// workgroup keeps the bytes through each CU small and spreads the work over
+// four times as many CUs as whole-batch workgroups would.
 // Per 32-deep step a wave loads its 16 weight columns (16 B per lane: 8 channels
 // of W_KV or of W_Z of one reduction row), transposes them through a private LDS
-// tile and reads its 4 token tiles' A operands straight from global memory; the
-// next step's loads are in flight during this step's MFMAs.
-constexpr int kFewTok = 64;   // tokens per workgroup
+// tile and reads the tile's A operand straight from global memory; the next
+// step's loads are in flight during this step's MFMA.
+constexpr int kFewTok = 64;   // tokens the kernel takes in all
 constexpr int kFewCh = 8;     // channels per workgroup
 constexpr int kFewTP = 40;    // LDS pitch (bf16) of a transposed weight column
 
@@ -286,33 +289,36 @@ template <int M, int NW>
 __global__ __launch_bounds__(64 * NW) void compress_few_kernel(
     const uint16_t* __restrict__ H, int n_tok, int d_model, const uint16_t* __restrict__ Wkv,
     const uint16_t* __restrict__ Wz, int d, long long pos0, int rope_dim, double theta,
-    int n_per_seq, float* __restrict__ out) {
+    int n_per_seq, int n_cg, int n_tt, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[NW][16 * kFewTP];  // per wave: [column][k]
-  __shared__ __attribute__((aligned(16))) float part[NW][4 * 64 * 4];     // per wave: 4 tiles x 64 lanes x 4
+  __shared__ __attribute__((aligned(16))) float part[NW][64 * 4];         // per wave: 64 lanes x 4
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
-  // Workgroups go to the 8 XCDs round-robin by id.  Consecutive channel groups
-  // are placed on one XCD (when their count is a multiple of 8), so each
-  // 128-byte line of weights is fetched into one XCD's L2, not into all eight.
-  const int n_cg = gridDim.x;
-  const int cg = (n_cg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (n_cg >> 3) + (int)(blockIdx.x >> 3);
+  // Workgroups go to the 8 XCDs round-robin by id.  The token tiles of a
+  // channel group, and consecutive channel groups, are placed on one XCD (when
+  // the channel groups are a multiple of 8), so each 128-byte line of weights
+  // is fetched into one XCD's L2, not into all eight.
+  int cg, tt;
+  if (n_cg & 7) {
+    cg = (int)blockIdx.x / n_tt;
+    tt = (int)blockIdx.x - cg * n_tt;
+  } else {
+    const int k = (int)(blockIdx.x >> 3);
+    cg = (int)(blockIdx.x & 7) * (n_cg >> 3) + k / n_tt;
+    tt = k % n_tt;
+  }
   const int c0 = cg * kFewCh;
   const int kq = d_model / NW, k_lo = wave * kq;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   // weight loads: lane l = reduction row l/2 of the step, W_KV (l even) or W_Z (odd)
   const uint16_t* wsrc = ((lane & 1) ? Wz : Wkv) + (size_t)(k_lo + (lane >> 1)) * d + c0;
-  // A rows: token 16 rt + col (clamped: rows past n_tok repeat the last token and are never stored)
-  const uint16_t* hrow[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) hrow[rt] = H + (size_t)min(16 * rt + col, n_tok - 1) * d_model + k_lo + 8 * g;
-  u32x4 wv, ha[4], wv_n, ha_n[4];
-  auto load = [&](int s, u32x4& w, u32x4 (&h)[4]) {
+  // A rows: token 16 tt + col (clamped: rows past n_tok repeat the last token and are never stored)
+  const uint16_t* hrow = H + (size_t)min(16 * tt + col, n_tok - 1) * d_model + k_lo + 8 * g;
+  u32x4 wv, ha, wv_n, ha_n;
+  auto load = [&](int s, u32x4& w, u32x4& h) {
     w = *reinterpret_cast<const u32x4*>(wsrc + (size_t)s * 32 * d);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) h[rt] = *reinterpret_cast<const u32x4*>(hrow[rt] + 32 * s);
+    h = *reinterpret_cast<const u32x4*>(hrow + 32 * s);
   };
-  f32x4_t acc[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int n_steps = kq / 32;
   uint16_t* tile = wt[wave];
   load(0, wv, ha);
@@ -328,28 +334,23 @@ __global__ __launch_bounds__(64 * NW) void compress_few_kernel(
     // keeps the compiler from moving the read above the writes
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&tile[col * kFewTP + 8 * g]);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma16x16x32(as_bf16x8(make_uint4(ha[rt][0], ha[rt][1], ha[rt][2], ha[rt][3])), b, acc[rt]);
+    acc = mfma16x16x32(as_bf16x8(make_uint4(ha[0], ha[1], ha[2], ha[3])), b, acc);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is rewritten next step
     if (s + 1 < n_steps) {
       wv = wv_n;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) ha[rt] = ha_n[rt];
+      ha = ha_n;
     }
   }
   // ---- the NW partial tiles, added in wave order
-  float4* mine = reinterpret_cast<float4*>(part[wave]);
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) mine[rt * 64 + lane] = make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]);
+  reinterpret_cast<float4*>(part[wave])[lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   __syncthreads();
-  if (wave >= 4) return;
-  // wave w finishes token tile rt = w: lane holds tokens 16w + 4g + i of column col
+  if (wave != 0) return;
+  // lane holds tokens 16 tt + 4g + i of column col
   f32x4_t tot = f32x4_t{0.f, 0.f, 0.f, 0.f};
   {
-    const float4* p0 = reinterpret_cast<const float4*>(part[0]) + wave * 64 + lane;
     float4 a[NW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) a[w] = p0[w * 256];
+    for (int w = 0; w < NW; ++w) a[w] = reinterpret_cast<const float4*>(part[w])[lane];
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot += f32x4_t{a[w].x, a[w].y, a[w].z, a[w].w};
   }
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(64 * NW) void compress_few_kernel(
   for (int i = 0; i < 4; ++i) zv[i] = __shfl_xor(tot[i], 8);
   const bool is_c = col < 8;
   const int c = c0 + (col & 7);
-  const int t0 = 16 * wave + 4 * g;
+  const int t0 = 16 * tt + 4 * g;
 #pragma unroll
   for (int e = 0; e < 4 / M; ++e) {
     float zmax = zv[e * M];
@@ -402,10 +403,12 @@ hipError_t launch_compress(const void* H, bool bf16_in, int B, int T, int d_mode
   if (compress_mfma_ok(bf16_in, d_model, d, d_z) && (long long)B * T <= kFewTok && T % m == 0 &&
       d_model % 128 == 0 && d % kFewCh == 0) {
     const int nt = B * T;
+    const int n_cg = d / kFewCh, n_tt = (nt + 15) / 16;
 #define CSA2_FEW(M_, NW_)                                                                             \
-  hipLaunchKernelGGL((compress_few_kernel<M_, NW_>), dim3(d / kFewCh), dim3(64 * NW_), 0, st,         \
+  hipLaunchKernelGGL((compress_few_kernel<M_, NW_>), dim3(n_cg * n_tt), dim3(64 * NW_), 0, st,        \
                      static_cast<const uint16_t*>(H), nt, d_model, static_cast<const uint16_t*>(W_kv), \
-                     static_cast<const uint16_t*>(W_z), d, pos0, rope_dim, rope_theta, n_ent, kv_out)
+                     static_cast<const uint16_t*>(W_z), d, pos0, rope_dim, rope_theta, n_ent, n_cg, n_tt, \
+                     kv_out)
     if (d_model % (32 * 16) == 0) {
       if (m == 1) CSA2_FEW(1, 16);
       else if (m == 2) CSA2_FEW(2, 16);
