@@ -77,3 +77,50 @@ def test_decode_full_size_sampled(name, attn_layers):
                                        synth.swa_tokens(wl, li, b))
                 attn_close(out, ref)
         print(f"[fullsize] {name}: sequence {b} checked", flush=True)
+
+
+def test_multi_query_full_size_sampled():
+    """The multi-query decode step at its benchmark size and launch configuration
+    (64 sequences x 65,536 entries, 6 queries per sequence, graph replay): on the
+    first and last sequence, every query's scores on a sampled range, its Full
+    Top-K over all entries, Reuse, and the attention of every layer over its
+    selection and its window up to the query's own position."""
+    from helpers import score_tol
+    bench, bd, sch = mods()
+    wl = synth.workload("mtp_64k_b64")
+    print(f"[fullsize] {wl.name}: B={wl.B} N={wl.N} Tq={wl.Tq}", flush=True)
+    codes, scales, kidx, layers = bench.build_inputs(wl, torch, bd, sch)
+    run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
+                             Tq=wl.Tq)
+    P = wl.N * wl.m
+    q_pos = (P + torch.arange(wl.Tq, dtype=torch.int32, device="cuda")).repeat(wl.B, 1)
+    swa_pos0, n_win = P + wl.Tq - wl.S, wl.S - wl.Tq + 1
+    g = run.capture(codes, scales, kidx, layers, q_pos=q_pos, swa_pos0=swa_pos0, n_win=n_win)
+    g.replay()
+    torch.cuda.synchronize()
+    for b in (0, wl.B - 1):
+        c_b, s_b = codes[b].cpu().numpy(), scales[b].cpu().numpy()
+        k_b = host_bf16_bits(kidx[b])
+        gsc = run.scores[b].cpu().numpy()                       # [Tq, N] of the Full layer
+        lo = (104729 * (b + 1)) % (wl.N - 2048)
+        sel_prev = None
+        for li, mode in enumerate(wl.layers):
+            gsel = run.selection_of(li)[b].cpu().numpy()        # [Tq, K]
+            qm = synth.q_main(wl, li, b, wl.Tq)
+            sw = synth.swa_tokens(wl, li, b)
+            if mode == "F":
+                qi, w = synth.q_index(wl, li, b, wl.Tq), synth.head_weights(wl, li, b, wl.Tq)
+                for t in range(wl.Tq):
+                    ref = index_scores(qi[t], w[t], k_b)
+                    assert np.all(np.abs(gsc[t, lo:lo + 2048] - ref[lo:lo + 2048]) <=
+                                  score_tol(qi[t], w[t], k_b[lo:lo + 2048]))
+                    check_topk(gsel[t], ref, wl.K)
+            else:
+                assert np.array_equal(gsel, sel_prev)
+            sel_prev = gsel
+            out = run.out[li][b].cpu().numpy()
+            for t in range(wl.Tq):
+                ref = sparse_attention(qm[t], c_b, s_b, gsel[t], sw, q_pos=P + t,
+                                       swa_pos0=swa_pos0, n_win=n_win)
+                attn_close(out[t], ref)
+        print(f"[fullsize] {wl.name}: sequence {b} checked", flush=True)
