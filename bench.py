@@ -351,8 +351,8 @@ def append_main(args, wl, torch, bd):
     # algorithmic bytes of one call: entries in, W_ik in, codes + scales + keys out,
     # window KV in, window codes out
     nbytes = B * d * 4 + d * d_i * 2 + B * (d // 2 + d // 16 + 2 * d_i) + L * B * d * 4 + L * B * d
-    # the compressor at this shape (B sequences x m tokens), for context: its
-    # tiles are sized for prefill (256 tokens), so most of each tile is padding
+    # the compressor at this shape (B sequences x m tokens), timed separately for
+    # context: it makes the entries this call appends
     H = bf(synth.append_hidden(wl))
     Wkv_b, Wz_b = synth.compressor_weights(wl)
     Wkv, Wz = bf(Wkv_b), bf(Wz_b)

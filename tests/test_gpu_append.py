@@ -114,3 +114,55 @@ def test_append_from_hidden_states(m, bf16):
         assert np.array_equal(codes[b].cpu().numpy(), q.codes)
         assert np.array_equal(scales[b].cpu().numpy(), q.scales)
         assert np.array_equal(host_bf16_bits(kidx[b]), indexer_k(q.codes, q.scales, W))
+
+
+def test_append_full_size_sampled():
+    """The append at its benchmark size and launch configuration (64 sequences
+    into row 65,535 of 65,536-row caches, 20 windows of 128, graph replay), and
+    the compressor at that decode shape (64 sequences x 1 token of width 5,120,
+    bf16), checked on the first and last sequence: the appended row, key and
+    window slots bit-exact, the neighbouring row and slot untouched, the
+    compressed entry within 1e-4 of RMS."""
+    import synth
+    wl = synth.workload("append_b64")
+    B, d, d_i, L, S, cap = wl.B, wl.d, wl.d_i, len(wl.layers), wl.S, wl.N
+    print(f"[append] full size: B={B} cap={cap} windows {L} x {S}", flush=True)
+    codes = torch.full((B, cap, d // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((B, cap, d // 16), 0x5A, dtype=torch.uint8, device="cuda")
+    kidx = torch.full((B, cap, d_i), 0x1234, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    swa = torch.full((L, B, S, d), 0xC3, dtype=torch.uint8, device="cuda")
+    W = synth.w_ik(wl)
+    kv_h = np.stack([synth.main_kv(wl, b, cap - 1, cap)[0] for b in range(B)])
+    win_h = synth.new_token_window(wl)
+    kv, win, Wd = dev(kv_h), dev(win_h), dev_bf16(W)
+    row, slot = cap - 1, (cap - 1) % S
+    step = lambda: bd().csa2_cache_append(codes, scales, row, kv=kv, W_ik=Wd, k_idx=kidx, win=win,
+                                          swa=swa, slot=slot)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    Hb = synth.append_hidden(wl)                                  # bf16 bits [B, 1, d_model]
+    Wkv_b, Wz_b = synth.compressor_weights(wl)
+    kvo = bd().csa2_compress(dev_bf16(Hb), dev_bf16(Wkv_b), dev_bf16(Wz_b), wl.m, pos0=cap - wl.m)
+    torch.cuda.synchronize()
+    for b in (0, B - 1):
+        q8 = quant_fp4(kv_h[b:b + 1])
+        assert np.array_equal(codes[b, row].cpu().numpy(), q8.codes[0])
+        assert np.array_equal(scales[b, row].cpu().numpy(), q8.scales[0])
+        assert np.array_equal(host_bf16_bits(kidx[b, row]), indexer_k(q8.codes, q8.scales, W)[0])
+        assert np.all(codes[b, row - 1].cpu().numpy() == 0xA5)
+        assert np.all(host_bf16_bits(kidx[b, row - 1]) == 0x1234)
+        w_b = swa[:, b].cpu().numpy()                              # [L, S, d]
+        assert np.array_equal(w_b[:, slot], e4m3_encode(win_h[:, b]))
+        assert np.all(w_b[:, slot - 1] == 0xC3)
+        ref = compress(bf16_to_f64(Hb[b]), bf16_to_f64(Wkv_b), bf16_to_f64(Wz_b), wl.m, pos0=cap - wl.m)
+        got = kvo[b].cpu().numpy()
+        assert np.max(np.abs(got - ref)) <= 1e-4 * np.sqrt(np.mean(ref ** 2))
+    print("[append] full size: sequences 0 and 63 checked", flush=True)
