@@ -159,16 +159,21 @@ def time_scan(wl, torch, bd, kidx, layers, reps):
     return e0.elapsed_time(e1) / reps / 1e3  # seconds
 
 
+def oracle_threads() -> int:
+    """Threads the oracle's numpy runs on (its BLAS thread pool; 1 if unknown)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(wl, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload: the
     decode step of 2 sequences, repeated until `seconds` of CPU work."""
     import synth
     from oracle.csa2 import LayerInputs, decode_step, indexer_k, quant_fp4
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = oracle_threads()
     from oracle.csa2 import swa_window_rows
     W = synth.w_ik(wl)
     P, S = wl.N * wl.m, wl.S
@@ -400,7 +405,7 @@ def append_main(args, wl, torch, bd):
             e4m3_encode(win_h)
             n += 1
         el = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": n * B / el, "unit": "tokens/s", "cores": os.cpu_count(),
+        out["cpu_baseline"] = {"value": n * B / el, "unit": "tokens/s", "cores": oracle_threads(),
                                "kind": "oracle",
                                "sample": f"{n} appends of all {B} sequences (quantise, key, window), "
                                          f"{el:.1f}s, float64 numpy"}
