@@ -219,6 +219,53 @@ def prefill_flops(wl) -> dict:
     return {"indexer": idx, "attention": attn, "compressor": comp, "visible_pairs": vis}
 
 
+def prefill_cpu_baseline(wl, seconds):
+    """The oracle, as it stands, on a bounded sample of the prefill chunk: the
+    chunk's entries are compressed (float64), quantised with the cached prefix and
+    given their keys in untimed setup; then the chunk's last 64 query rows go
+    through the per-query path (scores of every visible entry, Top-K, attention
+    in every layer) until `seconds` of CPU work."""
+    import synth
+    from oracle.codecs import bf16_to_f64
+    from oracle.csa2 import (compress, index_scores, indexer_k, quant_fp4, sparse_attention, topk,
+                             visible_count)
+    f = bf16_to_f64 if wl.h_dtype == "bf16" else (lambda a: a)
+    Wkv, Wz = synth.compressor_weights(wl)
+    kv_new = compress(f(synth.hidden(wl)), f(Wkv), f(Wz), wl.m, pos0=wl.pos0,
+                      rope_dim=wl.rope_dim).astype(np.float32)
+    pre, new = quant_fp4(synth.main_kv(wl, 0, 0, wl.n_pre)), quant_fp4(kv_new)
+    codes = np.concatenate([pre.codes, new.codes])
+    scales = np.concatenate([pre.scales, new.scales])
+    k = indexer_k(codes, scales, synth.w_ik(wl))
+    R, r0 = 64, wl.chunk - 64
+    inputs = []
+    for li, mode in enumerate(wl.layers):
+        qi = synth.q_index(wl, li, 0, R, r0) if mode == "F" else None
+        w = synth.head_weights(wl, li, 0, R, r0) if mode == "F" else None
+        inputs.append((synth.q_main(wl, li, 0, R, r0), synth.swa_tokens(wl, li, 0), qi, w))
+    none = np.full(wl.K, -1, dtype=np.int64)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        r = R - 1 - (n % R)
+        pos = wl.pos0 + r0 + r
+        nv = visible_count(pos, wl.N, wl.m)
+        sel = none
+        for mode, (qm, sw, qi, w) in zip(wl.layers, inputs):
+            if mode == "F":
+                sel = topk(index_scores(qi[r], w[r], k[:nv]), wl.K)
+            sparse_attention(qm[r], codes, scales, none if mode == "S" else sel, sw, q_pos=pos,
+                             swa_pos0=wl.swa_pos0, n_win=wl.n_win)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{n} query rows (the last 64 of the chunk, cycled) through scores of every "
+                      f"visible entry, Top-{wl.K} and attention in {len(wl.layers)} layers, {el:.1f}s, "
+                      f"float64 numpy; the chunk's compressor, quantisation and keys ran untimed "
+                      f"in setup"}
+
+
 def prefill_main(args, wl, torch, bd, sch):
     """One prefill chunk (compress, FP4 + indexer keys, Full + Reuse layers), from a
     captured graph; inputs resident in HBM.  value = chunk tokens / s."""
@@ -308,6 +355,9 @@ def prefill_main(args, wl, torch, bd, sch):
                      "launch_us": idx_s * 1e6, "algorithmic_flops_per_launch": fl["indexer"]},
         "chunk_flops": fl,
     }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = prefill_cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
