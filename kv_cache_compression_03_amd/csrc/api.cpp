@@ -175,6 +175,12 @@ CSA2_API int csa2_cache_append(const float* kv, int B, int d, long long cap, lon
     NEED_PTR(swa);
   }
   hipError_t e = hipSuccess;
+  if (kv && W_ik && csa2::cache_append_fused_ok(B, d, d_i, W_ik))   // one launch for all of it
+    return hip_status(csa2::launch_cache_append(kv, B, d, cap, row, codes, scales,
+                                                static_cast<const uint16_t*>(W_ik), d_i,
+                                                static_cast<uint16_t*>(k_idx), L > 0 ? win : nullptr, L,
+                                                S_, slot, swa_scale, swa, S(stream)),
+                      fn);
   if (kv) {
     e = csa2::launch_quant_fp4(kv, B, d, codes, scales, S(stream), cap, row);
     if (e == hipSuccess && W_ik)

@@ -18,6 +18,13 @@ hipError_t launch_indexer_k(const uint8_t* codes, const uint8_t* scales, long lo
                             const uint16_t* W_ik, int d_i, uint16_t* k_idx, hipStream_t st,
                             long long cap = 1, long long row = 0);
 // win [L, B, d] f32 -> E4M3 codes of win / swa_scale in swa[l][b][slot] ([L, B, S, d]).
+// quantiser + indexer keys + window encode of a decode-step append in one launch
+// (at most 256 entries, d <= 512, W_ik 16-byte aligned); win may be null (L = 0)
+bool cache_append_fused_ok(int B, int d, int d_i, const void* W_ik);
+hipError_t launch_cache_append(const float* kv, int B, int d, long long cap, long long row, uint8_t* codes,
+                               uint8_t* scales, const uint16_t* W_ik, int d_i, uint16_t* k_idx,
+                               const float* win, int L, int S, int slot, float swa_scale, uint8_t* swa,
+                               hipStream_t st);
 hipError_t launch_swa_append(const float* win, int L, int B, int S, int d, int slot, float swa_scale,
                              uint8_t* swa, hipStream_t st);
 
