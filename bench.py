@@ -380,6 +380,7 @@ def append_main(args, wl, torch, bd):
     kv_h = np.stack([synth.main_kv(wl, b, cap - 1, cap)[0] for b in range(B)])
     win_h = synth.new_token_window(wl)
     kv, win = torch.from_numpy(kv_h).to(dev), torch.from_numpy(win_h).to(dev)
+    copy_calibration(args, torch)
     # R appends per graph replay (rows N-R .. N-1, their window slots), as R decode
     # steps' appends would run: one replay per append would time the host's graph
     # launch rather than the device
@@ -448,7 +449,8 @@ def append_main(args, wl, torch, bd):
                    "appends_per_graph": R, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "cache_append_kernel (quantise, keys and window encode in one launch)",
                      "achieved": nbytes / step_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": nbytes / step_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": nbytes / step_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic_record(f"traffic_cache_append_{wl.name}.txt", "quant.hip", "common.h"),
                      "launch_us": step_s * 1e6, "algorithmic_bytes_per_launch": nbytes},
         "compress_at_this_shape_us": comp_s * 1e6,
     }
