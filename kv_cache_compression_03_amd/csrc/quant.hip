@@ -163,11 +163,14 @@ static inline size_t ik_few_lds_bytes(int d) {
 CSA2_DEV void ik_few_stage_w(const uint16_t* __restrict__ W, int DI, int c0, int d, uint16_t* ws) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kq = d / 4, k_lo = wave * kq;
+  // every load is made (an index past the wave's rows repeats its last chunk) and
+  // only the store is conditional, so buf stays in registers: with conditional
+  // loads the compiler kept it in scratch memory
   uint4 buf[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int t = i * 64 + lane;
-    if (t < kq * 4) buf[i] = *reinterpret_cast<const uint4*>(W + (size_t)(k_lo + (t >> 2)) * DI + c0 + 8 * (t & 3));
+    const int t = min(i * 64 + lane, kq * 4 - 1);
+    buf[i] = *reinterpret_cast<const uint4*>(W + (size_t)(k_lo + (t >> 2)) * DI + c0 + 8 * (t & 3));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
