@@ -182,6 +182,25 @@ CSA2_API int csa2_topk(const float* scores, int R, int N, const int* valid_len, 
                        int K, int* out_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_topk_noalloc -- csa2_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the scratch memory taken from
+ * a static device array of CSA2_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends.  The caller passes only inputs and
+ * outputs.  The array's address is looked up once per device, on the first call
+ * with that device current.  Nothing is allocated by this call.
+ *   Same arguments and limits as csa2_topk, without ws / ws_bytes.
+ *   Returns CSA2_ERR_WORKSPACE (before any launch) when csa2_topk_workspace(R, N,
+ *   K) exceeds CSA2_NOALLOC_SCRATCH_BYTES (about 480 rows of more than 16,384
+ *   entries at K = 512).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (two streams, two host threads) race and must be ordered by the caller.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+CSA2_API int csa2_topk_noalloc(const float* scores, int R, int N, const int* valid_len,
+                               const int* cand_map, int K, int* out_idx, void* stream);
+
+/*
  * csa2_index_reindex -- Reindex mode: rescore only the shared pool with this
  * layer's own indexer query and take a fresh Top-K inside it.
  * [deep-dive §3.2, §3.3; reading §4.2] shared main KV and indexer K, fresh

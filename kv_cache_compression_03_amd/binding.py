@@ -38,6 +38,7 @@ _SIGS = {
                          _c_p, _c_i, _c_i, _c_i, _c_p, _c_sz, _c_p], _c_i),
     "csa2_topk_workspace": ([_c_i, _c_i, _c_i], _c_sz),
     "csa2_topk": ([_c_p, _c_i, _c_i, _c_p, _c_p, _c_i, _c_p, _c_p, _c_sz, _c_p], _c_i),
+    "csa2_topk_noalloc": ([_c_p, _c_i, _c_i, _c_p, _c_p, _c_i, _c_p, _c_p], _c_i),
     "csa2_index_reindex_workspace": ([_c_i, _c_i, _c_i], _c_sz),
     "csa2_index_reindex": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_i, _c_p,
                             _c_p, _c_sz, _c_p], _c_i),
@@ -284,6 +285,24 @@ def csa2_topk(scores, K: int, valid_len=None, cand_map=None, out=None, ws=None, 
     ws = _ws(csa2_topk_workspace(R, N, K), scores, ws)
     _call("csa2_topk", _p(scores), R, N, _p(valid_len), _p(cand_map), K, _p(out), _p(ws),
           _nbytes(ws), _stream(stream))
+    return out
+
+
+def csa2_topk_noalloc(scores, K: int, out, valid_len=None, cand_map=None, stream=None):
+    """csa2_topk with its scratch in the library's static device array: nothing is
+    allocated, so `out` [R, K] int32 must be given."""
+    _dev(scores, "scores", F32)
+    N = scores.shape[-1]
+    R = scores.numel() // N if N else 0
+    if valid_len is not None:
+        _dev(valid_len, "valid_len", I32)
+    if cand_map is not None:
+        _dev(cand_map, "cand_map", I32)
+    _dev(out, "out", I32)
+    if out.numel() != R * K:
+        raise ValueError(f"out has {out.numel()} elements, expected {R * K}")
+    _call("csa2_topk_noalloc", _p(scores), R, N, _p(valid_len), _p(cand_map), K, _p(out),
+          _stream(stream))
     return out
 
 

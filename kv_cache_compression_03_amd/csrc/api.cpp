@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/csa2.h"
 #include "internal.h"
@@ -263,6 +264,70 @@ CSA2_API int csa2_topk(const float* scores, int R, int N, const int* valid_len, 
   OPT_PTR(ws);
   csa2::TopkWs tw{};
   if (need) tw = csa2::topk_ws_carve(ws, R, K);
+  return hip_status(csa2::launch_topk(scores, R, N, valid_len, cand_map, K, out_idx, tw, S(stream)), fn);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ Top-K without allocation
+
+// Scratch of csa2_topk_noalloc: one copy per GPU, held until the process ends.
+// On the host `scratch` names a host-side stand-in, never the device memory:
+// every use on the host goes through the address hipGetSymbolAddress returns for
+// the current device.
+static __device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up once per device).
+int scratch_address(void** out, const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CSA2_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  CHECK(dev >= 0 && dev < kMaxDevices, CSA2_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev,
+        kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CSA2_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+CSA2_API int csa2_topk_noalloc(const float* scores, int R, int N, const int* valid_len,
+                               const int* cand_map, int K, int* out_idx, void* stream) {
+  const char* fn = "csa2_topk_noalloc";
+  CHECK(R >= 0 && N >= 0, CSA2_ERR_INVALID_ARG, "%s: negative size", fn);
+  CHECK(K >= 1 && K <= 2048, CSA2_ERR_UNSUPPORTED, "%s: K must be in [1, 2048]", fn);
+  CHECK((long long)N < (1LL << 31) - 1 && R <= 65535, CSA2_ERR_INVALID_ARG, "%s: N or R too large", fn);
+  if (R == 0) return ok();
+  const size_t need = csa2_topk_workspace(R, N, K);
+  CHECK(need <= CSA2_NOALLOC_SCRATCH_BYTES, CSA2_ERR_WORKSPACE,
+        "%s: %d rows of %d entries need %zu bytes of scratch, the static array holds %zu", fn, R, N,
+        need, (size_t)CSA2_NOALLOC_SCRATCH_BYTES);
+  NEED_PTR(out_idx);
+  if (N > 0) NEED_PTR(scores);
+  OPT_PTR(valid_len);
+  OPT_PTR(cand_map);
+  csa2::TopkWs tw{};
+  if (need) {
+    void* base = nullptr;
+    const int st = scratch_address(&base, fn);
+    if (st != CSA2_OK) return st;
+    tw = csa2::topk_ws_carve(base, R, K);
+  }
   return hip_status(csa2::launch_topk(scores, R, N, valid_len, cand_map, K, out_idx, tw, S(stream)), fn);
 }
 
