@@ -227,9 +227,16 @@ CSA2_API int csa2_index_reindex(const void* q_idx, const float* w, const void* k
  *   q      [B, Tq, H_q, d] bf16
  *   codes  [B, N, d/2], scales [B, N, d/16]: the FP4 main KV
  *   sel    [B, Tq, K] int32 ascending entry indices, -1 padded
- *   swa    [B, S, d] E4M3 window tokens; token i sits at position swa_pos0 + i
+ *   swa    [B, S, d] E4M3 window tokens, a ring of S slots: the token at
+ *          position p >= swa_pos0 sits in slot (p - swa_pos0) mod S (a buffer
+ *          filled in order from swa_pos0 that has not wrapped is the linear case,
+ *          slot i = position swa_pos0 + i; csa2_cache_append's slot p mod S is the
+ *          ring with swa_pos0 = 0).
  *   q_pos  [B, Tq] int32 or NULL.  With positions, a query at t sees the window
- *          tokens at positions (t - n_win, t]; without, all S tokens.
+ *          tokens at positions max(t - n_win + 1, swa_pos0, t - S + 1) .. t; the
+ *          caller keeps every position a query can see in its slot (S >= n_win +
+ *          the number of later positions already written).  Without positions
+ *          every one of the S slots is visible.
  *   out    [B, Tq, H_q, d] f32;  lse [B, Tq, H_q] f32 natural-log sum-exp or NULL
  *   sm_scale <= 0 selects 1/sqrt(d).
  *   ws     >= csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) bytes

@@ -113,15 +113,8 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
   const int* srow = sel + (size_t)row * K;
   const int n_sel = N > 0 ? K : 0;
 
-  int swa_lo = 0, n_swa = S;
-  if (q_pos != nullptr) {
-    const long long t = q_pos[row];
-    long long lo = t - n_win + 1 - swa_pos0, hi = t - swa_pos0 + 1;
-    lo = lo < 0 ? 0 : lo;
-    hi = hi > S ? S : hi;
-    swa_lo = (int)lo;
-    n_swa = hi > lo ? (int)(hi - lo) : 0;
-  }
+  const WinRange win = window_of(q_pos, row, S, swa_pos0, n_win);
+  const int n_swa = win.n;
   // chunks hold keys of one kind: first the selected entries, then the window
   const int nm = (n_sel + kKC - 1) / kKC;
   const int n_chunks = nm + (n_swa + kKC - 1) / kKC;
@@ -156,7 +149,7 @@ __global__ __launch_bounds__(HG * 2 * 64) void sparse_attn_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int t = (c - nm) * kKC + 4 * kq + j;
-            const size_t tok = (size_t)b * S + swa_lo + (t < n_swa ? t : 0);
+            const size_t tok = (size_t)b * S + window_slot(win, t < n_swa ? t : 0, S);
             const uint2 raw = *reinterpret_cast<const uint2*>(swa + tok * D + 8 * dg);
             ra[it][j] = raw.x;
             rb[it][j] = raw.y;

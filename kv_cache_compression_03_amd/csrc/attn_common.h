@@ -35,6 +35,30 @@ static inline int xcd_grid(int rows, int per_row) {
   return rows < 8 ? rows * per_row : 8 * ((rows + 7) / 8) * per_row;
 }
 
+// The window buffer of a sequence is a ring of S slots: the token at position
+// p >= swa_pos0 sits in slot (p - swa_pos0) mod S (a buffer filled in order from
+// swa_pos0 that has not wrapped is the plain linear case).  A query at position t
+// sees positions max(t - n_win + 1, swa_pos0, t - S + 1) .. t: n consecutive
+// positions starting in slot `lo`, wrapping at S.  Without positions (decode)
+// every slot is visible.
+struct WinRange {
+  int lo, n;
+};
+CSA2_DEV WinRange window_of(const int* q_pos, int row, int S, long long swa_pos0, int n_win) {
+  if (q_pos == nullptr) return {0, S};
+  const long long t = q_pos[row];
+  long long lo = t - n_win + 1;
+  lo = lo < swa_pos0 ? swa_pos0 : lo;
+  lo = lo < t - S + 1 ? t - S + 1 : lo;
+  if (S <= 0 || t < lo) return {0, 0};
+  return {(int)((lo - swa_pos0) % S), (int)(t - lo + 1)};
+}
+// slot of the i-th visible window token (0 <= i < n <= S)
+CSA2_DEV int window_slot(const WinRange& w, int i, int S) {
+  const int s = w.lo + i;
+  return s >= S ? s - S : s;
+}
+
 // fp16 kernel (attn_f16.hip): 32-head groups, whole selection of a split staged;
 // hg2 = 32-head groups per workgroup (1 or 2, H_q / 32 a multiple of hg2).
 // Usable when H_q is a multiple of 32, d is 256 or 512 and 0 < swa_scale <= 128

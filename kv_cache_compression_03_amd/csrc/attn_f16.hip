@@ -120,15 +120,8 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
   // valid entry are masked, so no pass over the list is needed first
   const int* srow = sel + (size_t)row * K;
   const int n_sel = N > 0 ? K : 0;
-  int swa_lo = 0, n_swa = S;
-  if (q_pos != nullptr) {
-    const long long t = q_pos[row];
-    long long lo = t - n_win + 1 - swa_pos0, hi = t - swa_pos0 + 1;
-    lo = lo < 0 ? 0 : lo;
-    hi = hi > S ? S : hi;
-    swa_lo = (int)lo;
-    n_swa = hi > lo ? (int)(hi - lo) : 0;
-  }
+  const WinRange win = window_of(q_pos, row, S, swa_pos0, n_win);
+  const int n_swa = win.n;
   // chunks hold keys of one kind: first the selected entries, then the window
   const int nm = (n_sel + kKC - 1) / kKC;
   const int n_chunks = nm + (n_swa + kKC - 1) / kKC;
@@ -159,7 +152,7 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     const uint8_t* cb = codes + ent * (D / 2) + ((dseg * (VPT / 2)) & ~15);
     const uint8_t* sb = scales + ent * (D / 16) + ((dseg * NSB) & ~15);
     const int t = (c - nm) * kKC + dkey;
-    const uint8_t* wb = swa + ((size_t)b * S + swa_lo + (t >= 0 && t < n_swa ? t : 0)) * D + dseg * VPT;
+    const uint8_t* wb = swa + ((size_t)b * S + window_slot(win, t >= 0 && t < n_swa ? t : 0, S)) * D + dseg * VPT;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const uint8_t* m = i < NCL ? cb + 16 * i : sb;

@@ -358,11 +358,20 @@ def attend_lse(q, keys, sm_scale: Optional[float] = None) -> np.ndarray:
 def swa_window_rows(q_pos: Optional[int], S: int, swa_pos0: int, n_win: int) -> np.ndarray:
     """R14: the window is the n_win most recent tokens including the query's
     own: positions (t - n_win, t].  A decode query (q_pos None) sees the whole
-    window buffer."""
+    window buffer.
+
+    Buffer layout (reading R21): the buffer is a ring of S slots in which the
+    token at position p >= swa_pos0 sits in slot (p - swa_pos0) mod S, so it
+    holds at most the S most recent positions; a buffer filled in order from
+    swa_pos0 that has not wrapped is the linear case (slot i = position
+    swa_pos0 + i).  Returns the slots of the visible positions, oldest first:
+    positions max(t - n_win + 1, swa_pos0, t - S + 1) .. t."""
     if q_pos is None:
         return np.arange(S)
-    pos = swa_pos0 + np.arange(S)
-    return np.nonzero((pos <= q_pos) & (pos > q_pos - n_win))[0]
+    t = int(q_pos)
+    lo = max(t - n_win + 1, swa_pos0, t - S + 1)
+    pos = np.arange(lo, t + 1, dtype=np.int64)
+    return (pos - swa_pos0) % S if S > 0 else pos[:0]
 
 
 def sparse_attention(q, codes, scales, sel, swa_codes, swa_scale: float = 1.0,

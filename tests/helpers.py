@@ -55,3 +55,46 @@ def attn_close(out, ref):
     """Attention parity: max-abs error <= 2e-3 x RMS of the oracle output."""
     rms = np.sqrt(np.mean(np.asarray(ref) ** 2))
     assert np.max(np.abs(np.asarray(out) - ref)) <= 2e-3 * rms
+
+
+def _near(v, cut, rel):
+    return abs(v - cut) <= rel * abs(cut)
+
+
+def check_pool(gpu_pool, ref_scores, G, PB, PE, rel=1e-4, n_vis=None):
+    """Pool parity under the near-tie rule of the Top-K: the GPU pool (its valid
+    prefix) is strictly ascending; it holds min(PB, blocks) blocks, which are the
+    oracle's best blocks except where a differing block's maximum lies within
+    `rel` (relative) of the cut (the PB-th best block maximum); inside each of its
+    blocks it holds min(PE, block size) entries, the block's best ones except where
+    a differing entry's score lies within `rel` of that block's PE-th score.
+    Returns the number of exempt differences."""
+    s = np.asarray(ref_scores, dtype=np.float64)
+    n = s.shape[0] if n_vis is None else int(n_vis)
+    s = s[:n]
+    g = np.asarray(gpu_pool, dtype=np.int64)
+    assert np.all(np.diff(g) > 0), "pool must be strictly ascending"
+    assert g.size == 0 or (g[0] >= 0 and g[-1] < n), "pool entry outside the visible range"
+    nblk = -(-n // G)
+    bmax = np.array([s[b * G:min((b + 1) * G, n)].max() for b in range(nblk)])
+    nb = min(PB, nblk)
+    ref_blocks = np.lexsort((np.arange(nblk), -bmax))[:nb]
+    gblocks = np.unique(g // G)
+    assert gblocks.shape[0] == nb, f"{gblocks.shape[0]} blocks in the pool, expected {nb}"
+    exempt = 0
+    cut = np.sort(bmax)[::-1][nb - 1]
+    for b in set(gblocks.tolist()) ^ set(ref_blocks.tolist()):
+        assert _near(bmax[b], cut, rel), f"block {b}: max {bmax[b]} vs cut {cut}"
+        exempt += 1
+    for b in gblocks.tolist():
+        lo, hi = b * G, min((b + 1) * G, n)
+        ent = g[(g >= lo) & (g < hi)]
+        cnt = min(PE, hi - lo)
+        assert ent.shape[0] == cnt, f"block {b}: {ent.shape[0]} entries, expected {cnt}"
+        seg = s[lo:hi]
+        want = lo + np.lexsort((np.arange(hi - lo), -seg))[:cnt]
+        bcut = np.sort(seg)[::-1][cnt - 1]
+        for j in set(ent.tolist()) ^ set(want.tolist()):
+            assert _near(s[j], bcut, rel), f"entry {j}: score {s[j]} vs block cut {bcut}"
+            exempt += 1
+    return exempt

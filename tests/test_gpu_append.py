@@ -166,3 +166,48 @@ def test_append_full_size_sampled():
         got = kvo[b].cpu().numpy()
         assert np.max(np.abs(got - ref)) <= 1e-4 * np.sqrt(np.mean(ref ** 2))
     print("[append] full size: sequences 0 and 63 checked", flush=True)
+
+
+@pytest.mark.parametrize("H_q", [64, 48])
+def test_ring_window_after_wrap_multi_query(H_q):
+    """The window is a ring: csa2_cache_append writes the token at position p into
+    slot p mod S, and csa2_sparse_attn reads a query's window (t - n_win, t] from
+    the same slots.  Tokens are appended one at a time until the ring has wrapped
+    three times, then three queries at the last three positions (a token and two
+    drafted positions, S = n_win + 2) attend to their selections and windows; the
+    oracle attends over the linear history of window tokens (one row per position,
+    no ring)."""
+    from oracle.csa2 import sparse_attention
+    from helpers import attn_close
+    rng = np.random.default_rng(H_q)
+    B, d, n_win, Tq, N, K = 2, 512, 8, 3, 300, 16
+    S = n_win + Tq - 1
+    total = 3 * S + 4
+    win = rng.standard_normal((total, 1, B, d)).astype(np.float32)
+    ring = torch.full((1, B, S, d), 0xC3, dtype=torch.uint8, device="cuda")
+    codes = torch.zeros(B, 1, d // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(B, 1, d // 16, dtype=torch.uint8, device="cuda")
+    for p in range(total):
+        bd().csa2_cache_append(codes, scales, 0, win=dev(win[p]), swa=ring, slot=p % S)
+    hist = e4m3_encode(win[:, 0])                                   # [total, B, d]
+    r = ring.cpu().numpy()[0]
+    for b in range(B):
+        for p in range(total - S, total):
+            assert np.array_equal(r[b, p % S], hist[p, b]), "ring slot"
+    kv = rng.standard_normal((B, N, d)).astype(np.float32)
+    q8 = [quant_fp4(kv[b]) for b in range(B)]
+    cache_c = dev(np.stack([x.codes for x in q8]))
+    cache_s = dev(np.stack([x.scales for x in q8]))
+    sel = np.stack([np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(Tq)])
+                    for _ in range(B)]).astype(np.int32)
+    q = f64_to_bf16(rng.standard_normal((B, Tq, H_q, d)))
+    q_pos = np.broadcast_to(np.arange(total - Tq, total, dtype=np.int32), (B, Tq)).copy()
+    out = bd().csa2_sparse_attn(dev_bf16(q), cache_c, cache_s, dev(sel), ring[0].contiguous(),
+                                q_pos=dev(q_pos), swa_pos0=0, n_win=n_win)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            ref = sparse_attention(q[b, t], q8[b].codes, q8[b].scales, sel[b, t], hist[:, b],
+                                   q_pos=int(q_pos[b, t]), swa_pos0=0, n_win=n_win)
+            attn_close(out[b, t], ref)

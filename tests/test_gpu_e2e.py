@@ -5,9 +5,9 @@ import pytest
 import torch
 
 import synth
-from helpers import attn_close, check_topk, dev, dev_bf16, host_bf16_bits
+from helpers import attn_close, check_pool, check_topk, dev, dev_bf16, host_bf16_bits
 from oracle.csa2 import (LayerInputs, compress, decode_step, index_scores, indexer_k, quant_fp4,
-                         build_pool, reindex, sparse_attention, topk)
+                         sparse_attention)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,14 @@ def layer_inputs(wl, B, layers):
 
 def test_full_decode_4k_from_hidden_states():
     """One Full layer at 4K context: hidden states -> compressor (m = 2) -> FP4 + indexer
-    key -> scores -> Top-512 -> attention over 512 entries ++ 128 window tokens."""
+    key -> scores -> Top-512 -> attention over 512 entries ++ 128 window tokens.
+
+    Stage by stage, each oracle stage consuming the GPU's previous output: the
+    compressor against the oracle's; FP4 codes and scales of the GPU's entries
+    bit-exact; keys of the GPU's codes bit-exact; Top-K on the GPU's keys under
+    the near-tie rule; attention over the GPU's selection and cache, always.  The
+    independent oracle chain (its own compressor output) is also run, and its FP4
+    code mismatch rate (float64 vs float32 entries at rounding boundaries) bounded."""
     bd, sch = mods()
     wl = synth.workload("full_decode_4k")
     H = synth.hidden(wl)
@@ -54,19 +61,25 @@ def test_full_decode_4k_from_hidden_states():
     run = sch.DecodeSchedule(wl.layers, 1, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K)
     outs = run.step(codes, scales, kidx, devl)
     torch.cuda.synchronize()
-    # oracle chain
+    # compressor
     kv_ref = compress(H, Wkv, Wz, wl.m, rope_dim=wl.rope_dim)
     kv_gpu = kv.cpu().numpy()[0]
     assert np.max(np.abs(kv_gpu - kv_ref)) <= 1e-4 * np.sqrt(np.mean(kv_ref ** 2))
-    q8 = quant_fp4(kv_ref.astype(np.float32))
-    mism = (codes.cpu().numpy()[0] != q8.codes).mean() + (scales.cpu().numpy()[0] != q8.scales).mean()
-    assert mism <= 1e-4, mism  # float64 compressor: stored entries agree to float32 rounding
-    k_ref = indexer_k(q8.codes, q8.scales, Wik)
-    res = decode_step(wl.layers, host[0], q8.codes, q8.scales, k_ref, K=wl.K)
+    # FP4 of the GPU's entries, keys of the GPU's codes
+    codes_h, scales_h, kidx_h = codes.cpu().numpy()[0], scales.cpu().numpy()[0], host_bf16_bits(kidx)[0]
+    q8g = quant_fp4(kv_gpu)
+    assert np.array_equal(codes_h, q8g.codes) and np.array_equal(scales_h, q8g.scales)
+    assert np.array_equal(kidx_h, indexer_k(codes_h, scales_h, Wik))
+    # Top-K on the GPU's keys, attention on the GPU's selection
     sel = run.sel[0].cpu().numpy()[0, 0]
-    check_topk(sel, index_scores(host[0][0].q_idx, host[0][0].w, k_ref), wl.K)
-    if np.array_equal(sel, res.sel[0]) and mism == 0:
-        attn_close(outs[0].cpu().numpy()[0, 0], res.out[0])
+    check_topk(sel, index_scores(host[0][0].q_idx, host[0][0].w, kidx_h), wl.K)
+    attn_close(outs[0].cpu().numpy()[0, 0],
+               sparse_attention(host[0][0].q_main, codes_h, scales_h, sel, host[0][0].swa))
+    # the independent oracle chain: entries rounded from float64 differ from the
+    # GPU's float32 ones at most at rounding boundaries
+    q8 = quant_fp4(kv_ref.astype(np.float32))
+    mism = (codes_h != q8.codes).mean() + (scales_h != q8.scales).mean()
+    assert mism <= 1e-4, mism
 
 
 @pytest.mark.parametrize("sched", ["FUUU", "FURURU"])
@@ -95,25 +108,21 @@ def test_decode_schedule_small(sched):
         gpool = None
         if res.pool is not None:
             gpool = run.pool.cpu().numpy()[b, :run.pool_len[b].item()]
-            # near-ties of fp32 vs float64 scores may swap a block's 8th entry
-            assert len(set(gpool.tolist()) ^ set(res.pool.tolist())) <= 2
-        skipped = 0
+            assert np.all(run.pool.cpu().numpy()[b, run.pool_len[b].item():] == -1)
+            check_pool(gpool, res.full_scores, wl.G, wl.PB, wl.PE)
         for li, mode in enumerate(wl.layers):
             gsel = run.selection_of(li).cpu().numpy()[b, 0]
             li_in = host[b][li]
             if mode == "F":
                 check_topk(gsel, index_scores(li_in.q_idx, li_in.w, k_ref), wl.K)
-            elif mode == "R" and np.array_equal(gpool, res.pool):
-                check_topk(gsel, index_scores(li_in.q_idx, li_in.w, k_ref[res.pool]), wl.K,
-                           index_map=res.pool)
+            elif mode == "R":   # the oracle's Top-K over the GPU's own pool
+                check_topk(gsel, index_scores(li_in.q_idx, li_in.w, k_ref[gpool]), wl.K,
+                           index_map=gpool)
             elif mode == "U":
                 assert np.array_equal(gsel, run.selection_of(li - 1).cpu().numpy()[b, 0])
-            if np.array_equal(gsel, res.sel[li]):
-                attn_close(outs[li][b, 0], res.out[li])
-            else:
-                skipped += 1   # a near-tie changed the selection; attention itself is
-                               # checked on identical inputs in test_gpu_attn
-        assert skipped <= len(wl.layers) // 2
+            # attention over the GPU's selection, every layer
+            attn_close(outs[li][b, 0], sparse_attention(li_in.q_main, q8.codes, q8.scales, gsel,
+                                                        li_in.swa))
 
 
 def test_graph_replay_matches_eager():
@@ -163,35 +172,24 @@ def test_multi_query_decode(Tq, sched):
     outs = [o.cpu().numpy() for o in run.step(codes, scales, kidx, devl, q_pos=dev(q_pos),
                                                swa_pos0=swa_pos0, n_win=n_win)]
     codes_h, scales_h = codes.cpu().numpy(), scales.cpu().numpy()
-    compared = skipped = 0
     for b in range(B):
         q8 = quant_fp4(kv[b])
+        assert np.array_equal(codes_h[b], q8.codes) and np.array_equal(scales_h[b], q8.scales)
         k_ref = indexer_k(q8.codes, q8.scales, Wik)
-        last = None                                                # latest Full selections
         for li, mode in enumerate(sched):
             gsel = run.selection_of(li).cpu().numpy()[b]          # [Tq, K]
             if mode == "F":
-                wants = []
                 for t in range(Tq):
-                    s = index_scores(qi[li][b, t], ww[li][b, t], k_ref)
-                    check_topk(gsel[t], s, wl.K)
-                    wants.append(topk(s, wl.K))
-                last = wants
+                    check_topk(gsel[t], index_scores(qi[li][b, t], ww[li][b, t], k_ref), wl.K)
             elif mode == "U":
                 assert np.array_equal(gsel, run.selection_of(li - 1).cpu().numpy()[b])
-                wants = last
             else:
                 assert np.all(gsel == -1)
-                wants = list(gsel)
+            # every query's attention over the GPU's selection and its own window
             for t in range(Tq):
-                if not np.array_equal(gsel[t], wants[t]):
-                    skipped += 1                                  # a near-tie changed the selection
-                    continue
-                ref = sparse_attention(qm[li][b, t], codes_h[b], scales_h[b], wants[t], sw[li][b],
+                ref = sparse_attention(qm[li][b, t], codes_h[b], scales_h[b], gsel[t], sw[li][b],
                                        q_pos=int(q_pos[b, t]), swa_pos0=swa_pos0, n_win=n_win)
                 attn_close(outs[li][b, t], ref)
-                compared += 1
-    assert skipped <= compared // 4
 
 
 def test_full_layer_top_k_inside_the_pool():
@@ -211,25 +209,17 @@ def test_full_layer_top_k_inside_the_pool():
                              G=wl.G, PB=wl.PB, PE=wl.PE, full_in_pool=True)
     outs = [o.cpu().numpy() for o in run.step(codes, scales, kidx, devl)]
     codes_h, scales_h, kidx_h = codes.cpu().numpy(), scales.cpu().numpy(), host_bf16_bits(kidx)
-    compared = 0
     for b in range(B):
         li_in = host[b][0]
         s = index_scores(li_in.q_idx, li_in.w, kidx_h[b])
-        pool = build_pool(s, wl.G, wl.PB, wl.PE)
         gpool = run.pool.cpu().numpy()[b, :run.pool_len[b].item()]
-        assert len(set(gpool.tolist()) ^ set(pool.tolist())) <= 2
+        check_pool(gpool, s, wl.G, wl.PB, wl.PE)
         gsel = run.selection_of(0).cpu().numpy()[b, 0]
         assert set(gsel[gsel >= 0].tolist()) <= set(gpool.tolist())
-        if not np.array_equal(gpool, pool):
-            continue
-        check_topk(gsel, index_scores(li_in.q_idx, li_in.w, kidx_h[b][pool]), wl.K, index_map=pool)
-        want = reindex(li_in.q_idx, li_in.w, kidx_h[b], pool, wl.K)
+        # the oracle's Top-K inside the GPU's own pool
+        check_topk(gsel, index_scores(li_in.q_idx, li_in.w, kidx_h[b][gpool]), wl.K, index_map=gpool)
         for li in (1, 2):
             assert np.array_equal(run.selection_of(li).cpu().numpy()[b, 0], gsel)
-        if np.array_equal(gsel, want):
-            for li in range(len(wl.layers)):
-                ref = sparse_attention(host[b][li].q_main, codes_h[b], scales_h[b], want,
-                                       host[b][li].swa)
-                attn_close(outs[li][b, 0], ref)
-            compared += 1
-    assert compared >= 2
+        for li in range(len(wl.layers)):
+            ref = sparse_attention(host[b][li].q_main, codes_h[b], scales_h[b], gsel, host[b][li].swa)
+            attn_close(outs[li][b, 0], ref)

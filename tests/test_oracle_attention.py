@@ -97,3 +97,25 @@ def test_attend_lse_special_cases():
     assert np.allclose(shift, 2.0 * 3.0 / np.sqrt(8), atol=1e-12)
     # large logits do not overflow (max-shifted evaluation)
     assert np.isfinite(attend_lse(q * 1e4, k)).all()
+
+
+def test_window_rows_of_a_ring_match_the_linear_history():
+    """Reading R21 (window buffer as a ring): a ring of S slots written token by
+    token (each new position overwriting the oldest) must give every query the
+    same window tokens as the full linear history of positions gives it under
+    R14 (positions (t - n_win, t]), for queries up to the last written position
+    as long as the ring still holds their whole window."""
+    rng = np.random.default_rng(4)
+    n_win, d = 5, 3
+    hist = rng.integers(0, 120, (40, d)).astype(np.uint8)        # position p -> token
+    for S in (5, 7, 9):
+        ring = np.zeros((S, d), np.uint8)
+        for last in range(40):
+            ring[last % S] = hist[last]                            # append position `last`
+            for t in range(max(0, last - (S - n_win)), last + 1):  # whole window still held
+                got = ring[swa_window_rows(t, S, 0, n_win)]
+                lo = max(0, t - n_win + 1)
+                assert np.array_equal(got, hist[lo:t + 1]), (S, last, t)
+    # a linear buffer (no wrap) is the special case; an older start clips the window
+    assert list(swa_window_rows(7, 10, 5, 5)) == [0, 1, 2]
+    assert list(swa_window_rows(3, 10, 5, 5)) == []
