@@ -144,26 +144,39 @@ CSA2_API int csa2_cache_append(const float* kv, int B, int d, long long cap, lon
                                float swa_scale, uint8_t* swa, void* stream);
 
 /*
- * csa2_index_full -- Full-mode indexer: score every visible entry, and (first
- * Full layer of a decode step) build the shared candidate pool.
- * [deep-dive §3.1, §3.2] Indexer Q x Indexer K -> score;  reading: for query t,
- * s_j = sum_h w_h * max(0, q_h · k_j), accumulated in float32.
+ * csa2_index_full -- Full-mode indexer: score every visible entry, (first Full
+ * layer of a decode step) build the shared candidate pool, and take the layer's
+ * Top-K.
+ * [deep-dive §3.1, §3.2] Indexer Q x Indexer K -> score -> Top-K;  reading: for
+ * query t, s_j = sum_h w_h * max(0, q_h · k_j), accumulated in float32.
  * [deep-dive §3.3] the pool: blocks of G entries ranked by their best score,
  * the PB best blocks each give their PE best entries; union ascending.
+ * Readings: Top-K ranks by (score desc, index asc) over the visible entries, min(K,
+ * visible) of them, ascending, -1 padded; the Full layer's Top-K is global (not
+ * restricted to the pool).
  *   q_idx  [B, Tq, h_i, d_i] bf16;  w [B, Tq, h_i] f32;  k_idx [B, N, d_i] bf16
  *   q_pos  [B, Tq] int32 query positions, or NULL (decode: every entry visible);
  *          with positions, entry j is visible to a query at t iff (j+1)*m - 1 <= t.
  *   scores [B, Tq, N] f32 out (-inf where not visible)
  *   pool   [B*Tq, PB*PE] int32 out or NULL; pool_len [B*Tq] int32 out.
  *          Rows of the pool are ascending entry indices, -1 beyond pool_len.
- *   ws     >= csa2_index_full_workspace(B, Tq, N, G, PB, PE) bytes (0 without pool).
- * Limits: h_i in {4, 8, 16}, d_i in {64, 128}, G <= 256, PE <= 16, PB <= 2048.
+ *   sel    [B*Tq, K] int32 out or NULL: the Top-K of each query row.
+ *   ws     >= csa2_index_full_workspace(B, Tq, N, h_i, d_i, G, PB, PE, K) bytes (pass
+ *          G = 0 or PB = 0 without a pool, K = 0 without sel; 0 bytes when neither).
+ * With a pool or sel, a decode-shaped call (up to 1,048,576 entries, G = 128 for
+ * the pool) writes the maximum of every 16-entry tile beside the scores; the pool
+ * blocks and a provable lower bound of the K-th best score come from those
+ * maxima, so only the pool blocks and the blocks that can hold a Top-K entry are
+ * read again.
+ * Limits: h_i in {4, 8, 16}, d_i in {64, 128}, G <= 256, PE <= 16, PB <= 2048,
+ * K <= 2048.
  */
-CSA2_API size_t csa2_index_full_workspace(int B, int Tq, int N, int G, int PB, int PE);
+CSA2_API size_t csa2_index_full_workspace(int B, int Tq, int N, int h_i, int d_i, int G, int PB,
+                                          int PE, int K);
 CSA2_API int csa2_index_full(const void* q_idx, const float* w, const void* k_idx,
                              int B, int Tq, int N, int h_i, int d_i, const int* q_pos, int m,
                              float* scores, int* pool, int* pool_len, int G, int PB, int PE,
-                             void* ws, size_t ws_bytes, void* stream);
+                             int K, int* sel, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_topk -- the K best entries of each row.
@@ -239,7 +252,8 @@ CSA2_API int csa2_index_reindex(const void* q_idx, const float* w, const void* k
  *          every one of the S slots is visible.
  *   out    [B, Tq, H_q, d] f32;  lse [B, Tq, H_q] f32 natural-log sum-exp or NULL
  *   sm_scale <= 0 selects 1/sqrt(d).
- *   ws     >= csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) bytes
+ *   ws     >= csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) bytes (0 when a row is
+ *          not split over its keys)
  * Limits: d in {256, 512}, H_q % 16 == 0, K <= 2048.
  * Precision: products are exact (entries, window values and probabilities are
  * carried in fp16 or bf16, both exact for the decoded values) and accumulate in

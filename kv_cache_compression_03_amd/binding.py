@@ -33,9 +33,9 @@ _SIGS = {
     "csa2_indexer_keys": ([_c_p, _c_p, _c_ll, _c_i, _c_p, _c_i, _c_p, _c_p], _c_i),
     "csa2_cache_append": ([_c_p, _c_i, _c_i, _c_ll, _c_ll, _c_p, _c_p, _c_p, _c_i, _c_p, _c_p, _c_i,
                            _c_i, _c_i, _c_f, _c_p, _c_p], _c_i),
-    "csa2_index_full_workspace": ([_c_i, _c_i, _c_i, _c_i, _c_i, _c_i], _c_sz),
+    "csa2_index_full_workspace": ([_c_i, _c_i, _c_i, _c_i, _c_i, _c_i, _c_i, _c_i, _c_i], _c_sz),
     "csa2_index_full": ([_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_p, _c_i, _c_p, _c_p,
-                         _c_p, _c_i, _c_i, _c_i, _c_p, _c_sz, _c_p], _c_i),
+                         _c_p, _c_i, _c_i, _c_i, _c_i, _c_p, _c_p, _c_sz, _c_p], _c_i),
     "csa2_topk_workspace": ([_c_i, _c_i, _c_i], _c_sz),
     "csa2_topk": ([_c_p, _c_i, _c_i, _c_p, _c_p, _c_i, _c_p, _c_p, _c_sz, _c_p], _c_i),
     "csa2_topk_noalloc": ([_c_p, _c_i, _c_i, _c_p, _c_p, _c_i, _c_p, _c_p], _c_i),
@@ -148,8 +148,9 @@ def csa2_version() -> str:
     return lib().csa2_version().decode()
 
 
-def csa2_index_full_workspace(B, Tq, N, G=128, PB=2048, PE=8) -> int:
-    return lib().csa2_index_full_workspace(B, Tq, N, G, PB, PE)
+def csa2_index_full_workspace(B, Tq, N, h_i=8, d_i=128, G=128, PB=2048, PE=8, K=0) -> int:
+    """Workspace of csa2_index_full (G or PB = 0: no pool; K = 0: no Top-K)."""
+    return lib().csa2_index_full_workspace(B, Tq, N, h_i, d_i, G, PB, PE, K)
 
 
 def csa2_topk_workspace(R, N, K) -> int:
@@ -282,10 +283,12 @@ def csa2_cache_append(codes, scales, row: int, kv=None, W_ik=None, k_idx=None, w
 
 
 def csa2_index_full(q_idx, w, k_idx, q_pos=None, m: int = 1, scores=None, pool=None, pool_len=None,
-                    G: int = 128, PB: int = 2048, PE: int = 8, with_pool: bool = False, ws=None,
-                    stream=None):
+                    G: int = 128, PB: int = 2048, PE: int = 8, with_pool: bool = False, K: int = 0,
+                    sel=None, ws=None, stream=None):
     """q_idx [B, Tq, h_i, d_i] bf16, w [B, Tq, h_i] f32, k_idx [B, N, d_i] bf16 ->
-    scores [B, Tq, N] (and pool [B*Tq, PB*PE], pool_len [B*Tq] when with_pool)."""
+    scores [B, Tq, N]; with a pool (with_pool, or pool given) also pool [B*Tq, PB*PE]
+    and pool_len [B*Tq]; with K > 0 (or sel given) also the Full layer's Top-K
+    sel [B*Tq, K].  Returns scores, or a tuple (scores, [pool, pool_len,] [sel])."""
     _ndim(q_idx, "q_idx", 4)
     _chk(q_idx, "q_idx", BF16)
     B, Tq, h_i, d_i = q_idx.shape
@@ -302,6 +305,11 @@ def csa2_index_full(q_idx, w, k_idx, q_pos=None, m: int = 1, scores=None, pool=N
         _chk(pool, "pool", I32, numel=B * Tq * PB * PE)
     if pool_len is not None:
         _chk(pool_len, "pool_len", I32, numel=B * Tq)
+    if sel is not None:
+        if K <= 0:
+            raise ValueError("sel needs K > 0")
+        _chk(sel, "sel", I32, numel=B * Tq * K)
+    want_sel = K > 0
     _on_device(q_idx=q_idx)
     if scores is None:
         scores = torch.empty(B, Tq, N, dtype=torch.float32, device=q_idx.device)
@@ -310,12 +318,17 @@ def csa2_index_full(q_idx, w, k_idx, q_pos=None, m: int = 1, scores=None, pool=N
             pool = torch.empty(B * Tq, PB * PE, dtype=torch.int32, device=q_idx.device)
         if pool_len is None:
             pool_len = torch.empty(B * Tq, dtype=torch.int32, device=q_idx.device)
-        ws = _ws(csa2_index_full_workspace(B, Tq, N, G, PB, PE), q_idx, ws)
+    if want_sel and sel is None:
+        sel = torch.empty(B * Tq, K, dtype=torch.int32, device=q_idx.device)
+    ws = _ws(csa2_index_full_workspace(B, Tq, N, h_i, d_i, G if want_pool else 0,
+                                       PB if want_pool else 0, PE, K if want_sel else 0), q_idx, ws)
     _on_device(q_idx=q_idx, w=w, k_idx=k_idx, q_pos=q_pos, scores=scores, pool=pool,
-               pool_len=pool_len, ws=ws)
+               pool_len=pool_len, sel=sel, ws=ws)
     _call("csa2_index_full", _p(q_idx), _p(w), _p(k_idx), B, Tq, N, h_i, d_i, _p(q_pos), m,
-          _p(scores), _p(pool), _p(pool_len), G, PB, PE, _p(ws), _nbytes(ws), _stream(stream))
-    return (scores, pool, pool_len) if pool is not None else scores
+          _p(scores), _p(pool), _p(pool_len), G, PB, PE, K if want_sel else 0, _p(sel), _p(ws),
+          _nbytes(ws), _stream(stream))
+    out = (scores,) + ((pool, pool_len) if want_pool else ()) + ((sel,) if want_sel else ())
+    return out if len(out) > 1 else scores
 
 
 def _topk_args(scores, K, valid_len, cand_map, out):

@@ -198,16 +198,37 @@ static bool index_dims_ok(int h_i, int d_i) {
   return (h_i == 4 || h_i == 8 || h_i == 16) && (d_i == 64 || d_i == 128);
 }
 
-CSA2_API size_t csa2_index_full_workspace(int B, int Tq, int N, int G, int PB, int PE) {
+// Workspace of csa2_index_full for the way the call runs: the decode scan with
+// the Full-layer selection from its tile maxima, or the scores first and then the
+// separate pool and Top-K passes (prefill-shaped calls, other block sizes).
+static bool index_full_fused(int Tq, int N, int h_i, int d_i, int G, bool pool, bool sel) {
+  return (pool || sel) && !csa2::index_prefill_supported(Tq, N, h_i, d_i, nullptr) &&
+         csa2::full_select_supported(N, pool ? G : 128);
+}
+
+static size_t index_full_ws(int B, int Tq, int N, int h_i, int d_i, int G, int PB, int K, bool pool,
+                            bool sel) {
+  const int R = B * Tq;
+  if (!pool && !sel) return 0;
+  if (index_full_fused(Tq, N, h_i, d_i, G, pool, sel))
+    return csa2::full_select_ws_bytes(R, N, pool ? PB : 0, sel ? K : 0);
+  size_t a = pool ? csa2::pool_ws_bytes(R, N, G, PB) : 0;
+  size_t b = sel ? csa2::topk_ws_bytes(R, N, K) : 0;
+  return align256((size_t)R * sizeof(int)) + (a > b ? a : b);  // visible entries per row first
+}
+
+CSA2_API size_t csa2_index_full_workspace(int B, int Tq, int N, int h_i, int d_i, int G, int PB,
+                                          int PE, int K) {
   (void)PE;
-  if (B <= 0 || Tq <= 0 || N <= 0 || G <= 0 || PB <= 0) return 0;
-  return csa2::pool_ws_bytes(B * Tq, N, G, PB);
+  if (B <= 0 || Tq <= 0 || N <= 0) return 0;
+  const bool pool = G > 0 && PB > 0, sel = K > 0;
+  return index_full_ws(B, Tq, N, h_i, d_i, G, PB, K, pool, sel);
 }
 
 CSA2_API int csa2_index_full(const void* q_idx, const float* w, const void* k_idx, int B, int Tq,
                              int N, int h_i, int d_i, const int* q_pos, int m, float* scores,
-                             int* pool, int* pool_len, int G, int PB, int PE, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             int* pool, int* pool_len, int G, int PB, int PE, int K, int* sel,
+                             void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "csa2_index_full";
   CHECK(B >= 0 && Tq >= 0 && N >= 0, CSA2_ERR_INVALID_ARG, "%s: negative size", fn);
   CHECK(B <= 65535 && (long long)B * Tq <= 65535 && (long long)N < (1LL << 31) - 1,
@@ -219,11 +240,14 @@ CSA2_API int csa2_index_full(const void* q_idx, const float* w, const void* k_id
     CHECK(G >= 1 && G <= 256, CSA2_ERR_UNSUPPORTED, "%s: G must be in [1, 256]", fn);
     CHECK(PE >= 1 && PE <= 16, CSA2_ERR_UNSUPPORTED, "%s: PE must be in [1, 16]", fn);
     CHECK(PB >= 1 && PB <= 2048, CSA2_ERR_UNSUPPORTED, "%s: PB must be in [1, 2048]", fn);
-    const size_t need = csa2_index_full_workspace(B, Tq, N, G, PB, PE);
-    CHECK(ws_bytes >= need, CSA2_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-    CHECK(need == 0 || ws != nullptr, CSA2_ERR_WORKSPACE, "%s: workspace is null", fn);
-    OPT_PTR(ws);
   }
+  if (sel) CHECK(K >= 1 && K <= 2048, CSA2_ERR_UNSUPPORTED, "%s: K must be in [1, 2048]", fn);
+  const size_t need = (long long)B * Tq * N == 0
+                          ? 0
+                          : index_full_ws(B, Tq, N, h_i, d_i, G, PB, K, pool != nullptr, sel != nullptr);
+  CHECK(ws_bytes >= need, CSA2_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  CHECK(need == 0 || ws != nullptr, CSA2_ERR_WORKSPACE, "%s: workspace is null", fn);
+  OPT_PTR(ws);
   if ((long long)B * Tq * N == 0) return ok();
   NEED_PTR(q_idx);
   NEED_PTR(w);
@@ -232,11 +256,33 @@ CSA2_API int csa2_index_full(const void* q_idx, const float* w, const void* k_id
   OPT_PTR(q_pos);
   OPT_PTR(pool);
   OPT_PTR(pool_len);
-  hipError_t e = csa2::launch_index_scores(static_cast<const uint16_t*>(q_idx), w,
-                                           static_cast<const uint16_t*>(k_idx), nullptr, nullptr,
-                                           q_pos, m, B, Tq, N, N, h_i, d_i, scores, S(stream));
-  if (e == hipSuccess && pool)
-    e = csa2::launch_pool(scores, B * Tq, N, q_pos, m, G, PB, PE, pool, pool_len, ws, S(stream));
+  OPT_PTR(sel);
+  const int R = B * Tq;
+  const auto* q16 = static_cast<const uint16_t*>(q_idx);
+  const auto* k16 = static_cast<const uint16_t*>(k_idx);
+  if (index_full_fused(Tq, N, h_i, d_i, G, pool != nullptr, sel != nullptr)) {
+    // decode scan writing tile maxima, then pool and Top-K from them
+    hipError_t e = csa2::launch_index_scores(q16, w, k16, nullptr, nullptr, q_pos, m, B, Tq, N, N, h_i,
+                                             d_i, scores, S(stream), csa2::full_select_tmax(ws));
+    if (e == hipSuccess)
+      e = csa2::launch_full_select(scores, R, N, q_pos, m, pool ? PB : 0, PE, pool, pool_len,
+                                   sel ? K : 0, sel, ws, S(stream));
+    return hip_status(e, fn);
+  }
+  hipError_t e = csa2::launch_index_scores(q16, w, k16, nullptr, nullptr, q_pos, m, B, Tq, N, N, h_i,
+                                           d_i, scores, S(stream));
+  if (e == hipSuccess && pool) {
+    char* base = static_cast<char*>(ws) + align256((size_t)R * sizeof(int));
+    e = csa2::launch_pool(scores, R, N, q_pos, m, G, PB, PE, pool, pool_len, base, S(stream));
+  }
+  if (e == hipSuccess && sel) {
+    int* vlen = static_cast<int*>(ws);
+    e = csa2::launch_visible_len(q_pos, m, R, N, vlen, S(stream));
+    csa2::TopkWs tw{};
+    if (e == hipSuccess && csa2::topk_ws_bytes(R, N, K))
+      tw = csa2::topk_ws_carve(static_cast<char*>(ws) + align256((size_t)R * sizeof(int)), R, K);
+    if (e == hipSuccess) e = csa2::launch_topk(scores, R, N, vlen, nullptr, K, sel, tw, S(stream));
+  }
   return hip_status(e, fn);
 }
 

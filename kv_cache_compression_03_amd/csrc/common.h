@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #define CSA2_DEV __device__ __forceinline__
+#define CSA2_HOST_DEV __host__ __device__
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -153,6 +154,16 @@ CSA2_DEV int wave_reduce_i32(int v, Op op) {
   const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
   const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
   return op(op(a, b), op(c, d));
+}
+// Maximum over each 16-lane row of the wave, in every lane of the row (DPP only).
+CSA2_DEV float row16_max(float v) {
+  auto mx = [](int x, int y) { return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y))); };
+  int x = __float_as_int(v);
+  x = mx(x, dpp_mov<kDppQuadXor1>(x));
+  x = mx(x, dpp_mov<kDppQuadXor2>(x));
+  x = mx(x, dpp_mov<kDppRowRor4>(x));
+  x = mx(x, dpp_mov<kDppRowRor8>(x));
+  return __int_as_float(x);
 }
 CSA2_DEV float wave_max(float v) {
   return __int_as_float(wave_reduce_i32(__float_as_int(v), [](int x, int y) {

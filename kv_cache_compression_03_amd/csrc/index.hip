@@ -27,18 +27,21 @@ constexpr int kScanWaves = 4;
 #define CSA2_SCAN_TARGET_WGS 65536
 #endif
 constexpr int kScanBatch = CSA2_SCAN_BATCH;  // entry tiles whose keys are in flight together
+static_assert(kScanBatch * 16 == kTmaxSpan, "one score maximum per batch of tiles");
 
 // QG query tiles per wave (several queries per sequence, e.g. drafted positions):
 // each key tile is loaded once and multiplied by all of them.
-template <int HI, int DI, int QG>
-__global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
+// TM: also write the maximum of every 16-entry tile of each score row.
+template <int HI, int DI, int QG, bool TM>
+__global__ __launch_bounds__(kScanWaves * 64, QG == 1 ? 7 : 1) void index_scores_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, const int* __restrict__ gather,
     const int* __restrict__ gather_len, const int* __restrict__ q_pos, int m, int Tq, int N, int L,
-    int tiles_per_wave, float* __restrict__ scores) {
+    int tiles_per_wave, float* __restrict__ scores, float* __restrict__ tmax) {
   constexpr int QPT = 16 / HI;     // queries per A tile
   constexpr int KS = DI / 32;      // MFMA reduction steps
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: keep it (and the entry range) in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g = lane >> 4;
   const int b = blockIdx.z;
   const int tw0 = blockIdx.y * QG * QPT;   // first query of this workgroup
@@ -107,6 +110,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
         for (int s = 0; s < KS; ++s) kv[u][s] = kr[s * 4 + g];
       }
     }
+    float bm[QG];  // TM: this lane's maximum over the batch's tiles, per query tile
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) bm[qg] = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) {
       if (tile + u >= tiles_per_wave) break;
@@ -121,7 +127,27 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
         for (int i = 0; i < 4; ++i) v = fmaf(wr[qg][i], fmaxf(acc[i], 0.0f), v);
         if (HI >= 8) v += __shfl_xor(v, 16);
         if (HI >= 16) v += __shfl_xor(v, 32);
-        if (writer[qg] && e < L) srow[qg][e] = (ent_ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
+        const float sv = (ent_ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
+        if (writer[qg] && e < L) srow[qg][e] = sv;
+        if constexpr (TM) bm[qg] = fmaxf(bm[qg], e < L ? sv : -INFINITY);
+      }
+    }
+    if constexpr (TM) {
+      // the maximum of the batch's 32 entries for each query row: the 16 columns
+      // of a query are one 16-lane row of the wave
+      const int nmt = (L + kTmaxSpan - 1) / kTmaxSpan;
+      const int mt = (int)((wave_first + (long long)tile * 16) / kTmaxSpan);
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        const float tv = row16_max(bm[qg]);
+        // query row qi of the tile sits in lane row qi * HI / 4: its maximum is taken
+        // to a scalar and stored by lane 0 (uniform addresses, few vector registers)
+#pragma unroll
+        for (int qi = 0; qi < QPT; ++qi) {
+          const int t = tw0 + qg * QPT + qi;
+          const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), 16 * qi * (HI / 4 >= 1 ? HI / 4 : 1)));
+          if (lane == 0 && t < Tq && mt < nmt) tmax[((size_t)b * Tq + t) * nmt + mt] = v;
+        }
       }
     }
   }
@@ -130,9 +156,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scores_kernel(
 hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                                const int* gather, const int* gather_len, const int* q_pos, int m,
                                int B, int Tq, int N, int L, int h_i, int d_i, float* scores,
-                               hipStream_t st) {
+                               hipStream_t st, float* tmax) {
   if (B == 0 || Tq == 0 || L == 0) return hipSuccess;
-  if (L == N && index_prefill_supported(Tq, N, h_i, d_i, gather))
+  if (tmax == nullptr && L == N && index_prefill_supported(Tq, N, h_i, d_i, gather))
     return launch_index_prefill(q_idx, w, k_idx, q_pos, m, B, Tq, N, h_i, d_i, scores, st);
   const int qpt = 16 / h_i;
   const int qtiles = (Tq + qpt - 1) / qpt;
@@ -147,9 +173,15 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   tpw = (tpw + kScanBatch - 1) / kScanBatch * kScanBatch;
   const long long bx = (tiles + (long long)tpw * kScanWaves - 1) / ((long long)tpw * kScanWaves);
   dim3 grid((unsigned)bx, (unsigned)qgroups, (unsigned)B), block(kScanWaves * 64);
-#define CSA2_SCAN_Q(HI_, DI_, QG_)                                                                   \
-  hipLaunchKernelGGL((index_scores_kernel<HI_, DI_, QG_>), grid, block, 0, st, q_idx, w, k_idx, gather, \
-                     gather_len, q_pos, m, Tq, N, L, tpw, scores)
+#define CSA2_SCAN_Q(HI_, DI_, QG_)                                                                     \
+  do {                                                                                                  \
+    if (tmax)                                                                                           \
+      hipLaunchKernelGGL((index_scores_kernel<HI_, DI_, QG_, true>), grid, block, 0, st, q_idx, w, k_idx, \
+                         gather, gather_len, q_pos, m, Tq, N, L, tpw, scores, tmax);                    \
+    else                                                                                                \
+      hipLaunchKernelGGL((index_scores_kernel<HI_, DI_, QG_, false>), grid, block, 0, st, q_idx, w,     \
+                         k_idx, gather, gather_len, q_pos, m, Tq, N, L, tpw, scores, tmax);             \
+  } while (0)
 #define CSA2_SCAN(HI_, DI_)                     \
   do {                                          \
     if (qg == 1) CSA2_SCAN_Q(HI_, DI_, 1);      \

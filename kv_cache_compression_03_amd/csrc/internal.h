@@ -9,6 +9,7 @@
 namespace csa2 {
 
 constexpr int kTopkCap = 8192;  // candidates a Top-K row sorts in LDS
+constexpr int kTmaxSpan = 32;   // entries per score maximum the decode scan writes
 
 // quant.hip
 // Entry e of the input goes to cache row e * cap + row (defaults: contiguous).
@@ -40,10 +41,13 @@ bool index_prefill_supported(int Tq, int N, int h_i, int d_i, const int* gather)
 hipError_t launch_index_prefill(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                                 const int* q_pos, int m, int B, int Tq, int N, int h_i, int d_i,
                                 float* scores, hipStream_t st);
+// tmax (optional): [B*Tq, ceil(L/kTmaxSpan)] maxima of each kTmaxSpan-entry span of
+// every score row (-inf entries included), written with the scores; it takes the
+// decode scan even for many queries.
 hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                                const int* gather, const int* gather_len, const int* q_pos, int m,
                                int B, int Tq, int N, int L, int h_i, int d_i, float* scores,
-                               hipStream_t st);
+                               hipStream_t st, float* tmax = nullptr);
 
 // topk.hip
 struct TopkWs {
@@ -61,6 +65,19 @@ hipError_t launch_topk(const float* scores, int R, int N, const int* valid_len, 
 size_t pool_ws_bytes(int R, int N, int G, int PB);
 hipError_t launch_pool(const float* scores, int R, int N, const int* q_pos, int m, int G, int PB,
                        int PE, int* pool, int* pool_len, void* ws, hipStream_t st);
+
+// Full-layer selection from the decode scan's tile maxima (topk.hip): the pool
+// (PB best 128-entry blocks, PE best entries each; pool may be null) and the
+// Top-K (sel [R, K]; may be null) of every row, visibility from q_pos / m.  The
+// workspace starts with the tile maxima the scan writes (full_select_tmax).
+bool full_select_supported(int N, int G);
+size_t full_select_ws_bytes(int R, int N, int PB, int K);
+float* full_select_tmax(void* ws);
+hipError_t launch_full_select(const float* scores, int R, int N, const int* q_pos, int m, int PB,
+                              int PE, int* pool, int* pool_len, int K, int* sel, void* ws,
+                              hipStream_t st);
+// vlen[r] = entries visible to row r (q_pos null: N)
+hipError_t launch_visible_len(const int* q_pos, int m, int R, int N, int* vlen, hipStream_t st);
 
 // attn.hip
 struct AttnPlan {

@@ -381,7 +381,7 @@ CSA2_DEV void pad_chosen(int* chosen, int k) {
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int N, const int* __restrict__ valid_len,
     const int* __restrict__ cand_map, int K, int* __restrict__ out, const int* __restrict__ cnt,
-    const float* __restrict__ cscore, const int* __restrict__ cidx) {
+    int cnt_stride, const float* __restrict__ cscore, const int* __restrict__ cidx) {
   extern __shared__ unsigned long long keys[];  // kTopkCap keys (64 KB)
   __shared__ __attribute__((aligned(16))) int chosen[2048];
   __shared__ uint32_t hist[512];
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int r = blockIdx.x, tid = threadIdx.x;
   const int n = row_len(valid_len, r, N);
   const bool direct = n <= kTopkCap;
-  const int total = direct ? n : cnt[r];
+  const int total = direct ? n : cnt[(size_t)r * cnt_stride];
   const int k = min(K, n);
   const float* row = scores + (size_t)r * N;
   if (!direct && (total > kTopkCap || total < k)) {
@@ -429,6 +429,87 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   write_ranked(chosen, k, K, out + (size_t)r * K, cand_map ? cand_map + (size_t)r * N : nullptr);
 }
 
+// A key T with at least k of the workgroup's keys >= T (NPT keys per thread; key 0
+// marks an empty slot and ranks below every real key).  Radix select by 8-bit
+// digits from the highest bit where the keys differ; with `passes` >= 4 (or when
+// a digit's bucket is taken whole) T is exactly the k-th largest key, otherwise
+// it is the k-th largest key with its remaining low bits cleared (a lower bound).
+// hist: 256 uint32 of LDS; bc: 4 uint32 of LDS.  k >= 1.
+template <int NPT>
+CSA2_DEV uint32_t block_kth_u32(const uint32_t (&key)[NPT], int k, int passes, uint32_t* hist,
+                                uint32_t* bc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t kor = 0u, kand = ~0u;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    kor |= key[i];
+    kand &= key[i] ? key[i] : ~0u;
+  }
+  if (tid == 0) {
+    bc[0] = 0u;
+    bc[1] = ~0u;
+  }
+  __syncthreads();
+  {
+    const uint32_t o = (uint32_t)wave_reduce_i32((int)kor, [](int x, int y) { return x | y; });
+    const uint32_t a = (uint32_t)wave_reduce_i32((int)kand, [](int x, int y) { return x & y; });
+    if (lane == 0) {
+      atomicOr(&bc[0], o);
+      atomicAnd(&bc[1], a);
+    }
+  }
+  __syncthreads();
+  const uint32_t diff = bc[0] ^ bc[1];
+  __syncthreads();
+  int top = diff ? 31 - __clz((int)diff) : 0;  // highest bit where (non-empty) keys differ
+  uint32_t mask = top >= 31 ? 0u : ~0u << (top + 1);
+  uint32_t prefix = bc[1] & mask;
+  int need = k;
+  for (int pass = 0, shift = top - 7; shift > -8; shift -= 8, ++pass) {
+    if (shift < 0) shift = 0;
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if ((key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t hv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[q] = hist[4 * lane + q];
+      const int c = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+      int suf = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o);
+        if (lane + o < 64) suf += y;
+      }
+      int run = suf - c;  // keys in buckets above this lane's
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (run < need && run + (int)hv[q] >= need) {  // one bucket of one lane
+          bc[2] = (uint32_t)(4 * lane + q);
+          bc[3] = (uint32_t)(need - run) | ((uint32_t)hv[q] << 16);
+        }
+        run += (int)hv[q];
+      }
+      // fewer keys than k under the prefix (the first pass, when k exceeds the
+      // number of non-empty keys): every key is taken, T = 0
+      if (lane == 0 && suf < need) bc[2] = 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    const uint32_t dsel = bc[2], nb = bc[3];
+    __syncthreads();
+    if (dsel == 0xFFFFFFFFu) return 0u;
+    prefix |= dsel << shift;
+    mask |= 255u << shift;
+    const int need2 = (int)(nb & 0xFFFFu), bucket = (int)(nb >> 16);
+    need = need2;
+    if (bucket == need || shift == 0 || pass + 1 >= passes) break;
+  }
+  return prefix;
+}
+
 // Rows of at most kRowCap entries (prefill: thousands of rows of 12K-16K visible
 // entries) in one pass, one workgroup per row: the row is staged in LDS, the
 // minimum T of C >= K chunk maxima bounds the K-th best score from below, the
@@ -448,7 +529,6 @@ __global__ __launch_bounds__(kSelThreads, 8) void topk_row_kernel(
   __shared__ uint32_t hist[512];
   __shared__ unsigned long long bcast[8];
   __shared__ int misc[32];
-  __shared__ float red[kSelThreads / 64];
   __shared__ uint32_t bitmap[kRowCap / 32];
   __shared__ int wsum[kSelThreads / 64];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -475,9 +555,11 @@ __global__ __launch_bounds__(kSelThreads, 8) void topk_row_kernel(
   } else {
     // The row stays in registers (thread t holds entries t + 1024u).  Chunks are
     // sets of a thread's entries: any C >= K disjoint non-empty chunks have C
-    // distinct maxima, so the K-th best score is at least the smallest of them.
-    // C = 512 chunks (threads t and t + 512 together) when K <= 512, else one
-    // chunk per thread (C = 1024) or per half of a thread's entries (C = 2048).
+    // distinct maxima, so at least K entries score >= the K-th largest chunk
+    // maximum, which therefore bounds the K-th best score from below.  C = 1024
+    // chunks (one per thread) when K <= 1024, else 2048 (one per half of a
+    // thread's entries); the bound is the K-th largest maximum with its key's low
+    // bits cleared after two radix digits.
     float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -486,25 +568,17 @@ __global__ __launch_bounds__(kSelThreads, 8) void topk_row_kernel(
       if (u < kPer / 2) m0 = fmaxf(m0, v);
       else m1 = fmaxf(m1, v);
     }
-    float cm;  // this thread's share of min over chunk maxima
-    if (K <= kSelThreads / 2) {
-      float* pm = reinterpret_cast<float*>(keys);  // keys are written only later
-      pm[tid] = fmaxf(m0, m1);
-      __syncthreads();
-      cm = tid < kSelThreads / 2 ? fmaxf(pm[tid], pm[tid + kSelThreads / 2]) : INFINITY;
-    } else if (K <= kSelThreads) {
-      cm = fmaxf(m0, m1);
+    uint32_t ck[2];  // chunk maxima as keys; 0 = empty chunk
+    if (K <= kSelThreads) {
+      ck[0] = tid < n ? mono_key(fmaxf(m0, m1)) : 0u;
+      ck[1] = 0u;
     } else {
-      cm = fminf(m0, m1);  // an empty half (max -inf) sends the row to the exact path below
+      ck[0] = tid < n ? mono_key(m0) : 0u;
+      ck[1] = tid + kSelThreads * (kPer / 2) < n ? mono_key(m1) : 0u;
     }
+    const uint32_t tk = block_kth_u32<2>(ck, k, 2, hist, reinterpret_cast<uint32_t*>(misc + 16));
     if (tid == 0) misc[0] = 0;
-    cm = wave_min(cm);
-    if (lane == 0) red[wave] = cm;
     __syncthreads();
-    float T = red[0];
-#pragma unroll
-    for (int w2 = 1; w2 < kSelThreads / 64; ++w2) T = fminf(T, red[w2]);
-    const uint32_t tk = mono_key(T);
     // the wave's candidates of all kPer rounds take one slot range (one atomic);
     // the ballots are taken again for the placement rather than kept (sixteen
     // 64-bit masks in scalar registers would cost the second workgroup per CU)
@@ -600,13 +674,14 @@ hipError_t launch_topk(const float* scores, int R, int N, const int* valid_len, 
   }
   hipLaunchKernelGGL(topk_select_kernel, dim3(R), dim3(kSelThreads),
                      kTopkCap * sizeof(unsigned long long), st, scores, N, valid_len, cand_map, K,
-                     out_idx, ws.cnt, ws.cscore, ws.cidx);
+                     out_idx, ws.cnt, 1, ws.cscore, ws.cidx);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- candidate pool
 
 static inline int pool_nblk(int N, int G) { return (N + G - 1) / G; }
+
 
 size_t pool_ws_bytes(int R, int N, int G, int PB) {
   const int nb = pool_nblk(N, G);
@@ -665,34 +740,14 @@ __global__ __launch_bounds__(256) void pool_blockmax_kernel(const float* __restr
 }
 
 
-// Per selected block, its PE best entries (score, then lower index) in ascending
-// index order.  One wave per block, KPL = ceil(G/64) keys per lane; each pick is
-// an arg-max over the wave: the 32-bit score key is reduced first, and the full
-// (score, index) key only when several lanes tie on the score.
+// The PE best entries (score, then lower index) of row[lo, lo + len), len <= 64 *
+// KPL, written in ascending index order to out[0 .. min(PE, len)) and -1 to the
+// rest of out[0 .. PE).  One wave; each pick is an arg-max over the wave: the
+// 32-bit score key is reduced first, the full (score, index) key only when
+// several lanes tie on the score.
 template <int KPL>
-__global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restrict__ scores, int N,
-                                                          const int* __restrict__ q_pos, int m, int G,
-                                                          int PB, int PE,
-                                                          const int* __restrict__ selblk,
-                                                          int* __restrict__ pool,
-                                                          int* __restrict__ pool_len) {
-  const int r = blockIdx.y;
+CSA2_DEV void block_top_pe(const float* __restrict__ row, int lo, int len, int PE, int* out) {
   const int lane = threadIdx.x & 63;
-  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (slot >= PB) return;
-  const int n = visible(q_pos, m, r, N);
-  const int nblk = (n + G - 1) / G;
-  const int nsel = min(PB, nblk);
-  int* prow = pool + (size_t)r * PB * PE;
-  if (slot >= nsel) {
-    for (int i = lane; i < PE; i += 64) prow[(size_t)slot * PE + i] = -1;
-    if (slot == 0 && lane == 0) pool_len[r] = 0;
-    return;
-  }
-  const int blk = selblk[(size_t)r * PB + slot];
-  const int lo = blk * G;
-  const int len = min(G, n - lo);
-  const float* row = scores + (size_t)r * N;
   unsigned long long key[KPL];  // 0 = no entry (a real key is never 0)
 #pragma unroll
   for (int q = 0; q < KPL; ++q) {
@@ -731,9 +786,39 @@ __global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restric
     const int v = __builtin_amdgcn_readlane(mine, q);
     rank += (q < cntb && v < mine) ? 1 : 0;
   }
-  if (lane < cntb) prow[(size_t)slot * PE + rank] = mine;
-  else if (lane < PE) prow[(size_t)slot * PE + lane] = -1;
-  if (slot == nsel - 1 && lane == 0) pool_len[r] = slot * PE + cntb;
+  if (lane < cntb) out[rank] = mine;
+  else if (lane < PE) out[lane] = -1;
+}
+
+// Per selected block, its PE best entries (score, then lower index) in ascending
+// index order.  One wave per block, KPL = ceil(G/64) keys per lane; each pick is
+// an arg-max over the wave: the 32-bit score key is reduced first, and the full
+// (score, index) key only when several lanes tie on the score.
+template <int KPL>
+__global__ __launch_bounds__(256) void pool_gather_kernel(const float* __restrict__ scores, int N,
+                                                          const int* __restrict__ q_pos, int m, int G,
+                                                          int PB, int PE,
+                                                          const int* __restrict__ selblk,
+                                                          int* __restrict__ pool,
+                                                          int* __restrict__ pool_len) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= PB) return;
+  const int n = visible(q_pos, m, r, N);
+  const int nblk = (n + G - 1) / G;
+  const int nsel = min(PB, nblk);
+  int* prow = pool + (size_t)r * PB * PE;
+  if (slot >= nsel) {
+    for (int i = lane; i < PE; i += 64) prow[(size_t)slot * PE + i] = -1;
+    if (slot == 0 && lane == 0) pool_len[r] = 0;
+    return;
+  }
+  const int blk = selblk[(size_t)r * PB + slot];
+  const int lo = blk * G;
+  const int len = min(G, n - lo);
+  block_top_pe<KPL>(scores + (size_t)r * N, lo, len, PE, prow + (size_t)slot * PE);
+  if (slot == nsel - 1 && threadIdx.x % 64 == 0) pool_len[r] = slot * PE + min(PE, len);
 }
 
 hipError_t launch_pool(const float* scores, int R, int N, const int* q_pos, int m, int G, int PB,
@@ -763,6 +848,473 @@ hipError_t launch_pool(const float* scores, int R, int N, const int* q_pos, int 
   else
     hipLaunchKernelGGL(pool_gather_kernel<4>, ggrid, dim3(256), 0, st, scores, N, q_pos, m, G, PB, PE,
                        selblk, pool, pool_len);
+  return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------- Full-layer selection from tile maxima
+//
+// The decode scan writes, with the scores, the maximum of every 32-entry span of
+// each row.  From those maxima alone one workgroup per row (the plan kernel)
+// finds, for the whole visible range:
+//   * block maxima of the G = 128-entry pool blocks (4 spans each) and the PB
+//     best blocks by (maximum desc, block asc) -- the pool's blocks;
+//   * a threshold T for the Top-K: T is at most the K-th largest maximum of
+//     C >= K disjoint groups of spans; those K group maxima are K distinct entries
+//     scoring >= T, so the K-th best score is >= T, and every entry of the K best
+//     lies in a span whose maximum is >= T (the candidate spans).
+// A gather kernel then reads only the pool blocks (their PE best entries) and the
+// candidate spans (entries scoring >= T, appended to a candidate list), and the
+// exact select above finishes the Top-K from the candidates.  With 4,096 groups
+// per row the threshold keeps about K entries of a million.
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxBlocks = 8;  // pool blocks per thread: rows of up to 1,048,576 entries
+constexpr int kPlanGroups = 4;     // threshold groups per thread
+constexpr int kCntStride = 64;     // candidate counters one 256-byte line apart (per row)
+
+struct PlanWs {
+  uint32_t* thr;   // [R] threshold key (mono_key of T)
+  int* npb;        // [R] pool blocks chosen
+  int* nct;        // [R] candidate spans
+  int* vlen;       // [R] visible entries
+  int* selblk;     // [R, PB] pool blocks, ascending
+  int* candtile;   // [R, spans] candidate spans
+};
+
+// Inclusive prefix sum over the workgroup (kPlanThreads threads, one value each).
+// wsum: kPlanThreads / 64 ints of LDS.  Returns the inclusive prefix; *total the sum.
+CSA2_DEV int block_scan_incl(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();  // wsum may still be read by a previous scan
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kPlanThreads / 64; ++w2) {
+    const int c = wsum[w2];
+    before += w2 < wave ? c : 0;
+    tot += c;
+  }
+  *total = tot;
+  return before + x;
+}
+
+// Two radix selections over the workgroup's keys at once (they share every
+// barrier): for each, a key T with at least k keys >= T (key 0 marks an empty
+// slot and ranks below every real key), found digit by digit (8 bits) from the
+// highest bit where the non-empty keys differ.  Selection s stops after
+// passes[s] digits (T = the k-th largest key with its lower bits cleared: a lower
+// bound) or when its digit's bucket is taken whole; with 4 passes T is exact.
+// k[s] = 0 skips selection s (T = 0).  hist: 512 uint32 of LDS; bc: 16 uint32.
+template <int NA, int NB>
+CSA2_DEV void block_kth2_u32(const uint32_t (&ka)[NA], const uint32_t (&kb)[NB], const int (&k)[2],
+                             const int (&passes)[2], uint32_t (&T)[2], uint32_t* hist, uint32_t* bc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t kor[2] = {0u, 0u}, kand[2] = {~0u, ~0u};
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    kor[0] |= ka[i];
+    kand[0] &= ka[i] ? ka[i] : ~0u;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    kor[1] |= kb[i];
+    kand[1] &= kb[i] ? kb[i] : ~0u;
+  }
+  if (tid < 2) {
+    bc[2 * tid] = 0u;
+    bc[2 * tid + 1] = ~0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const uint32_t o = (uint32_t)wave_reduce_i32((int)kor[s2], [](int x, int y) { return x | y; });
+    const uint32_t a = (uint32_t)wave_reduce_i32((int)kand[s2], [](int x, int y) { return x & y; });
+    if (lane == 0) {
+      atomicOr(&bc[2 * s2], o);
+      atomicAnd(&bc[2 * s2 + 1], a);
+    }
+  }
+  __syncthreads();
+  uint32_t prefix[2], mask[2];
+  int shift[2], need[2];
+  bool live[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const uint32_t diff = bc[2 * s2] ^ bc[2 * s2 + 1];
+    const int top = diff ? 31 - __clz((int)diff) : 0;
+    mask[s2] = top >= 31 ? 0u : ~0u << (top + 1);
+    prefix[s2] = bc[2 * s2 + 1] & mask[s2];
+    shift[s2] = top - 7;
+    need[s2] = k[s2];
+    live[s2] = k[s2] > 0;
+    T[s2] = 0u;
+  }
+  __syncthreads();
+  for (int pass = 0; live[0] || live[1]; ++pass) {
+    int sh[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) sh[s2] = shift[s2] < 0 ? 0 : shift[s2];
+    if (tid < 512) hist[tid] = 0u;
+    __syncthreads();
+    if (live[0]) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+        if ((ka[i] & mask[0]) == prefix[0]) atomicAdd(&hist[(ka[i] >> sh[0]) & 255u], 1u);
+    }
+    if (live[1]) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if ((kb[i] & mask[1]) == prefix[1]) atomicAdd(&hist[256 + ((kb[i] >> sh[1]) & 255u)], 1u);
+    }
+    __syncthreads();
+    if (tid < 128) {  // wave s2 finds selection s2's bucket
+      const int s2 = tid >> 6;
+      if (live[s2]) {
+        const uint32_t* h = hist + 256 * s2;
+        uint32_t hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hv[q] = h[4 * lane + q];
+        const int c = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+        int suf = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_down(suf, o);
+          if (lane + o < 64) suf += y;
+        }
+        int run = suf - c;  // keys in buckets above this lane's
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          if (run < need[s2] && run + (int)hv[q] >= need[s2]) {  // one bucket of one lane
+            bc[8 + 2 * s2] = (uint32_t)(4 * lane + q);
+            bc[9 + 2 * s2] = (uint32_t)(need[s2] - run) | ((uint32_t)hv[q] << 16);
+          }
+          run += (int)hv[q];
+        }
+        // fewer keys than k under the prefix (first pass, k above the number of
+        // non-empty keys): every key is taken, T = 0
+        if (lane == 0 && suf < need[s2]) bc[8 + 2 * s2] = 0xFFFFFFFFu;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (!live[s2]) continue;
+      const uint32_t dsel = bc[8 + 2 * s2], nb = bc[9 + 2 * s2];
+      if (dsel == 0xFFFFFFFFu) {
+        T[s2] = 0u;
+        live[s2] = false;
+        continue;
+      }
+      prefix[s2] |= dsel << sh[s2];
+      mask[s2] |= 255u << sh[s2];
+      need[s2] = (int)(nb & 0xFFFFu);
+      const int bucket = (int)(nb >> 16);
+      T[s2] = prefix[s2];
+      if (bucket == need[s2] || sh[s2] == 0 || pass + 1 >= passes[s2]) live[s2] = false;
+      shift[s2] -= 8;
+    }
+    __syncthreads();
+  }
+}
+
+// Span maxima (kTmaxSpan = 32 entries each) of a row are read as float4 f =
+// j * kPlanThreads + t, j < F: every load instruction is coalesced, and float4 f
+// holds the four spans of pool block f (128 entries), so each thread owns F
+// blocks.
+template <int F>
+CSA2_DEV void plan_load(const float* __restrict__ trow, int ns, float4 (&v)[F]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < F; ++j) {
+    const int f = j * kPlanThreads + t, sp = 4 * f;
+    if (sp + 3 < ns) {
+      v[j] = reinterpret_cast<const float4*>(trow)[f];
+    } else {
+      v[j].x = sp < ns ? trow[sp] : -INFINITY;
+      v[j].y = sp + 1 < ns ? trow[sp + 1] : -INFINITY;
+      v[j].z = sp + 2 < ns ? trow[sp + 2] : -INFINITY;
+      v[j].w = sp + 3 < ns ? trow[sp + 3] : -INFINITY;
+    }
+  }
+}
+
+template <int F>
+__global__ __launch_bounds__(kPlanThreads) void select_plan_kernel(
+    const float* __restrict__ tmax, int L, const int* __restrict__ q_pos, int m, int K, int PB,
+    PlanWs pw, int* __restrict__ cnt) {
+  constexpr int NG = kPlanGroups;                      // threshold groups per thread
+  constexpr int GSP = 4 * F / NG;                      // spans per group
+  constexpr int kBlkWords = kPlanThreads * F / 32;     // bitmap words of all blocks
+  static_assert(kBlkWords <= kPlanThreads && GSP >= 1, "plan shape");
+  __shared__ uint32_t hist[512];
+  __shared__ uint32_t bc[16];
+  __shared__ int wsum[kPlanThreads / 64];
+  __shared__ uint32_t bitmap[kBlkWords];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int ns_cap = (L + kTmaxSpan - 1) / kTmaxSpan;
+  const int n = visible(q_pos, m, r, L);
+  const int ns = (n + kTmaxSpan - 1) / kTmaxSpan, nblk = (n + 127) / 128;
+  const float* trow = tmax + (size_t)r * ns_cap;
+  uint32_t gk[NG], bk[F];  // keys of threshold groups and pool blocks; 0 = empty
+  {
+    float4 v[F];
+    plan_load<F>(trow, ns, v);
+    float sm[4 * F];  // span maxima, local span l = 4j + c
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      sm[4 * j] = v[j].x;
+      sm[4 * j + 1] = v[j].y;
+      sm[4 * j + 2] = v[j].z;
+      sm[4 * j + 3] = v[j].w;
+      const float bm = fmaxf(fmaxf(v[j].x, v[j].y), fmaxf(v[j].z, v[j].w));
+      bk[j] = j * kPlanThreads + tid < nblk ? mono_key(bm) : 0u;
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float gm = -INFINITY;
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < GSP; ++u) {
+        const int l = g * GSP + u;
+        gm = fmaxf(gm, sm[l]);
+        any = any || 4 * ((l >> 2) * kPlanThreads + tid) + (l & 3) < ns;
+      }
+      gk[g] = any ? mono_key(gm) : 0u;
+    }
+  }
+  if (tid == 0) {
+    pw.vlen[r] = n;
+    if (cnt != nullptr) cnt[(size_t)r * kCntStride] = 0;
+  }
+  const int take = PB > 0 ? min(PB, nblk) : 0;
+  uint32_t T[2];
+  {
+    const int kk[2] = {K > 0 ? K : 0, take};
+    const int ps[2] = {2, 4};  // Top-K: a lower bound after two digits; pool: exact
+    block_kth2_u32<NG, F>(gk, bk, kk, ps, T, hist, bc);
+  }
+  const uint32_t thr = T[0], V = T[1];
+  // ---- candidate spans (maximum >= T): the span maxima again, from L2
+  unsigned long long cmask = 0ull;  // bit 4j + c: span 4(j*1024 + t) + c is a candidate
+  if (K > 0) {
+    float4 v[F];
+    plan_load<F>(trow, ns, v);
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int sp = 4 * (j * kPlanThreads + tid) + c;
+        if (sp < ns && mono_key(e[c]) >= thr) cmask |= 1ull << (4 * j + c);
+      }
+    }
+  }
+  const int ncand = __popcll(cmask);
+  int tot1;
+  const int pos0 = block_scan_incl(ncand, wsum, &tot1) - ncand;
+  {
+    int pos = pos0;
+    for (unsigned long long mm = cmask; mm; mm &= mm - 1ull) {
+      const int b = __ffsll((long long)mm) - 1;
+      pw.candtile[(size_t)r * ns_cap + pos++] = 4 * ((b >> 2) * kPlanThreads + tid) + (b & 3);
+    }
+  }
+  if (tid == 0) {
+    pw.thr[r] = thr;
+    pw.nct[r] = K > 0 ? tot1 : 0;
+    pw.npb[r] = take;
+  }
+  // ---- pool blocks: above V all, equal to V in block order until `take`; the
+  // equal blocks are ranked through a bitmap of block indices and the chosen
+  // blocks written ascending through a second one
+  if (take > 0) {
+    for (int w2 = tid; w2 < kBlkWords; w2 += kPlanThreads) bitmap[w2] = 0u;
+    __syncthreads();
+    int ngt = 0;
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      const int blk = j * kPlanThreads + tid;
+      if (bk[j] != 0u && bk[j] > V) ++ngt;
+      if (bk[j] != 0u && bk[j] == V) atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
+    }
+    int tgt;
+    block_scan_incl(ngt, wsum, &tgt);  // (its barriers also publish the bitmap)
+    const int need_eq = take - tgt;
+    const uint32_t word = tid < kBlkWords ? bitmap[tid] : 0u;
+    int wtot;
+    const int wbefore = block_scan_incl(__popc(word), wsum, &wtot) - __popc(word);
+    uint32_t keep = 0u;  // the first need_eq equal blocks
+    {
+      int rank = wbefore;
+      for (uint32_t mm = word; mm; mm &= mm - 1u) {
+        const int b = __ffs(mm) - 1;
+        if (rank++ < need_eq) keep |= 1u << b;
+      }
+    }
+    __syncthreads();
+    if (tid < kBlkWords) bitmap[tid] = keep;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      const int blk = j * kPlanThreads + tid;
+      if (bk[j] != 0u && bk[j] > V) atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
+    }
+    __syncthreads();
+    const uint32_t chosen = tid < kBlkWords ? bitmap[tid] : 0u;
+    int ptot;
+    int p = block_scan_incl(__popc(chosen), wsum, &ptot) - __popc(chosen);
+    for (uint32_t mm = chosen; mm; mm &= mm - 1u) pw.selblk[(size_t)r * PB + p++] = 32 * tid + __ffs(mm) - 1;
+  }
+}
+
+// Pool role: wave s of a row takes pool block s (its PE best entries to pool
+// slots s*PE ..).  Candidate role: the workgroup takes 8 candidate spans per
+// round (a lane per entry, two spans per wave); entries scoring >= T are
+// appended to the row's candidate list with one atomic per workgroup and round.
+template <int KPL>
+__global__ __launch_bounds__(256) void select_gather_kernel(
+    const float* __restrict__ scores, int L, int PB, int PE, PlanWs pw, int* __restrict__ pool,
+    int* __restrict__ pool_len, int* __restrict__ cnt, float* __restrict__ cscore,
+    int* __restrict__ cidx) {
+  __shared__ int s_cnt[4];
+  __shared__ int s_base;
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = blockIdx.x * 4 + wave;
+  const int n = pw.vlen[r];
+  const int ns_cap = (L + kTmaxSpan - 1) / kTmaxSpan;
+  const float* row = scores + (size_t)r * L;
+  if (PB > 0 && slot < PB) {
+    const int npb = pw.npb[r];
+    int* prow = pool + (size_t)r * PB * PE;
+    if (slot >= npb) {
+      for (int i = lane; i < PE; i += 64) prow[(size_t)slot * PE + i] = -1;
+      if (slot == 0 && lane == 0) pool_len[r] = 0;
+    } else {
+      const int blk = pw.selblk[(size_t)r * PB + slot];
+      const int lo = blk * 128, len = min(128, n - lo);
+      block_top_pe<KPL>(row, lo, len, PE, prow + (size_t)slot * PE);
+      if (slot == npb - 1 && lane == 0) pool_len[r] = slot * PE + min(PE, len);
+    }
+  }
+  const int nct = pw.nct[r];
+  const uint32_t thr = pw.thr[r];
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int c0 = blockIdx.x * 8; c0 < nct; c0 += gridDim.x * 8) {  // uniform per workgroup
+    const int c = c0 + 2 * wave + (lane >> 5);
+    const int sp = c < nct ? pw.candtile[(size_t)r * ns_cap + c] : -1;
+    const int i = sp * kTmaxSpan + (lane & 31);
+    const float v = (sp >= 0 && i < n) ? row[i] : -INFINITY;
+    const bool take = sp >= 0 && i < n && mono_key(v) >= thr;
+    const unsigned long long mk = __ballot(take);
+    if (lane == 0) s_cnt[wave] = __popcll(mk);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int tot = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+      s_base = tot ? atomicAdd(&cnt[(size_t)r * kCntStride], tot) : 0;
+    }
+    __syncthreads();
+    int p = s_base;
+    for (int w2 = 0; w2 < wave; ++w2) p += s_cnt[w2];
+    p += __popcll(mk & below);
+    if (take && p < kTopkCap) {
+      cscore[(size_t)r * kTopkCap + p] = v;
+      cidx[(size_t)r * kTopkCap + p] = i;
+    }
+    __syncthreads();  // s_cnt / s_base are rewritten next round
+  }
+}
+
+size_t full_select_ws_bytes(int R, int N, int PB, int K) {
+  const size_t nt = (size_t)(N + kTmaxSpan - 1) / kTmaxSpan;
+  size_t b = 0;
+  b += align256((size_t)R * nt * sizeof(float));                 // span maxima
+  b += 4 * align256((size_t)R * sizeof(int));                     // thr, npb, nct, vlen
+  b += align256((size_t)R * (PB > 0 ? PB : 1) * sizeof(int));     // pool blocks
+  b += align256((size_t)R * nt * sizeof(int));                    // candidate spans
+  if (K > 0) {
+    b += align256((size_t)R * kCntStride * sizeof(int));          // candidate counters
+    b += 2 * align256((size_t)R * kTopkCap * sizeof(float));      // candidates
+  }
+  return b;
+}
+
+float* full_select_tmax(void* ws) { return static_cast<float*>(ws); }
+
+bool full_select_supported(int N, int G) {
+  return N <= kPlanThreads * kPlanMaxBlocks * 128 && G == 128;
+}
+
+hipError_t launch_full_select(const float* scores, int R, int N, const int* q_pos, int m, int PB,
+                              int PE, int* pool, int* pool_len, int K, int* sel, void* ws,
+                              hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  char* p = static_cast<char*>(ws);
+  const size_t nt = (size_t)(N + kTmaxSpan - 1) / kTmaxSpan;
+  const float* tmax = reinterpret_cast<const float*>(p);
+  p += align256((size_t)R * nt * sizeof(float));
+  PlanWs pw;
+  pw.thr = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)R * sizeof(int));
+  pw.npb = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * sizeof(int));
+  pw.nct = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * sizeof(int));
+  pw.vlen = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * sizeof(int));
+  pw.selblk = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * (PB > 0 ? PB : 1) * sizeof(int));
+  pw.candtile = reinterpret_cast<int*>(p);
+  p += align256((size_t)R * nt * sizeof(int));
+  int* cnt = nullptr;
+  float* cscore = nullptr;
+  int* cidx = nullptr;
+  if (K > 0) {
+    cnt = reinterpret_cast<int*>(p);
+    p += align256((size_t)R * kCntStride * sizeof(int));
+    cscore = reinterpret_cast<float*>(p);
+    p += align256((size_t)R * kTopkCap * sizeof(float));
+    cidx = reinterpret_cast<int*>(p);
+  }
+  const int pb = pool ? PB : 0;
+  const int nblk = (N + 127) / 128;
+#define CSA2_PLAN(F_)                                                                             \
+  hipLaunchKernelGGL(select_plan_kernel<F_>, dim3(R), dim3(kPlanThreads), 0, st, tmax, N, q_pos, m, \
+                     sel ? K : 0, pb, pw, cnt)
+  if (nblk <= kPlanThreads) CSA2_PLAN(1);
+  else if (nblk <= 2 * kPlanThreads) CSA2_PLAN(2);
+  else if (nblk <= 4 * kPlanThreads) CSA2_PLAN(4);
+  else CSA2_PLAN(8);
+#undef CSA2_PLAN
+  // pool: one wave per pool block; candidates: 8 spans per workgroup and round
+  const int wgs = max((pb + 3) / 4, 64);
+  hipLaunchKernelGGL(select_gather_kernel<2>, dim3(wgs, R), dim3(256), 0, st, scores, N, pb, PE, pw,
+                     pool, pool_len, cnt, cscore, cidx);
+  if (sel)
+    hipLaunchKernelGGL(topk_select_kernel, dim3(R), dim3(kSelThreads),
+                       kTopkCap * sizeof(unsigned long long), st, scores, N, pw.vlen, nullptr, K, sel,
+                       cnt, kCntStride, cscore, cidx);
+  return hipGetLastError();
+}
+
+// Entries visible to each row (decode: all N; with positions: floor((t+1)/m)).
+__global__ void visible_len_kernel(const int* __restrict__ q_pos, int m, int R, int N,
+                                   int* __restrict__ vlen) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < R) vlen[r] = visible(q_pos, m, r, N);
+}
+
+hipError_t launch_visible_len(const int* q_pos, int m, int R, int N, int* vlen, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  hipLaunchKernelGGL(visible_len_kernel, dim3((R + 255) / 256), dim3(256), 0, st, q_pos, m, R, N, vlen);
   return hipGetLastError();
 }
 

@@ -72,11 +72,13 @@ class DecodeSchedule:
         self.pool = torch.empty(B, PB * PE, **i32) if self.need_pool else None
         self.pool_len = torch.empty(B, **i32) if self.need_pool else None
         self.out = [torch.empty(B, Tq, H_q, d, dtype=torch.float32, device=dev) for _ in self.layers]
-        ws = max(bd.csa2_index_full_workspace(B, Tq, N, G, PB, PE) if self.need_pool else 0,
-                 bd.csa2_topk_workspace(B * Tq, N, K),
-                 bd.csa2_index_reindex_workspace(B, PB * PE, K) if self.need_pool else 0,
-                 bd.csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S))
+        ws = max(bd.csa2_index_full_workspace(B, Tq, N, h_i, d_i, G if self.need_pool else 0,
+                                              PB if self.need_pool else 0, PE,
+                                              0 if full_in_pool else K),
+                 bd.csa2_index_reindex_workspace(B, PB * PE, K) if self.need_pool else 0)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.empty(max(bd.csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S), 256),
+                                   dtype=torch.uint8, device=dev)
 
     def selection_of(self, layer: int) -> torch.Tensor:
         """The selection layer `layer` attends to (Reuse: the most recent Full/Reindex)."""
@@ -98,25 +100,27 @@ class DecodeSchedule:
         for i, (mode, lb) in enumerate(zip(self.layers, layers)):
             if mode == FULL:
                 build = (self.need_pool and not pool_built) or self.full_in_pool
+                # scores, the pool (first Full layer) and, unless it is taken inside
+                # the pool, the layer's Top-K in one call
                 bd.csa2_index_full(lb.q_idx, lb.w, k_idx, scores=self.scores,
                                    pool=self.pool if build else None,
                                    pool_len=self.pool_len if build else None,
-                                   G=self.G, PB=self.PB, PE=self.PE, ws=self.ws, stream=stream)
+                                   G=self.G, PB=self.PB, PE=self.PE,
+                                   K=0 if self.full_in_pool else K,
+                                   sel=None if self.full_in_pool else self.sel[i].view(R, K),
+                                   ws=self.ws, stream=stream)
                 pool_built = pool_built or build
                 if self.full_in_pool:   # the Top-K inside the pool this layer just built
                     bd.csa2_index_reindex(lb.q_idx.view(B, self.h_i, self.d_i), lb.w.view(B, self.h_i),
                                           k_idx, self.pool, self.pool_len, K,
                                           sel=self.sel[i].view(B, K), ws=self.ws, stream=stream)
-                else:
-                    bd.csa2_topk(self.scores.view(R, self.N), K, out=self.sel[i].view(R, K),
-                                 ws=self.ws, stream=stream)
             elif mode == REINDEX:
                 bd.csa2_index_reindex(lb.q_idx.view(B, self.h_i, self.d_i), lb.w.view(B, self.h_i),
                                       k_idx, self.pool, self.pool_len, K,
                                       sel=self.sel[i].view(B, K), ws=self.ws, stream=stream)
             bd.csa2_sparse_attn(lb.q_main, codes, scales, self.selection_of(i), lb.swa,
                                 swa_scale=self.swa_scale, q_pos=q_pos, swa_pos0=swa_pos0,
-                                n_win=n_win, out=self.out[i], ws=self.ws, stream=stream)
+                                n_win=n_win, out=self.out[i], ws=self.attn_ws, stream=stream)
         return self.out
 
     def capture(self, codes, scales, k_idx, layers, warmup: int = 1, **step_kw) -> torch.cuda.CUDAGraph:
@@ -169,15 +173,15 @@ class PrefillChunk:
         self.n_new = Tq // m
         self.kv_new = torch.empty(1, self.n_new, d, dtype=torch.float32, device=dev)
         self.q_pos = torch.arange(pos0, pos0 + Tq, **i32).view(1, Tq)
-        # entries visible to each query: floor((t + 1) / m), at most N
-        self.valid_len = torch.clamp((self.q_pos.view(Tq) + 1) // m, max=N).to(torch.int32)
         self.scores = torch.empty(1, Tq, N, dtype=torch.float32, device=dev)
         self.sel: Dict[int, torch.Tensor] = {i: torch.empty(1, Tq, K, **i32)
                                              for i, mo in enumerate(self.layers) if mo == FULL}
         self.no_sel = torch.full((1, Tq, K), -1, **i32)
         self.out = [torch.empty(1, Tq, H_q, d, dtype=torch.float32, device=dev) for _ in self.layers]
-        ws = max(bd.csa2_topk_workspace(Tq, N, K), bd.csa2_sparse_attn_workspace(1, Tq, H_q, d, K, S))
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(bd.csa2_index_full_workspace(1, Tq, N, h_i, d_i, 0, 0, 8, K), 256),
+                              dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.empty(max(bd.csa2_sparse_attn_workspace(1, Tq, H_q, d, K, S), 256),
+                                   dtype=torch.uint8, device=dev)
 
     def selection_of(self, layer: int) -> torch.Tensor:
         if self.layers[layer] == SWA_ONLY:
@@ -199,11 +203,11 @@ class PrefillChunk:
                           k_idx=k_idx[0, lo:hi], stream=stream)
         for i, (mode, lb) in enumerate(zip(self.layers, layers)):
             if mode == FULL:
+                # causal scores and each query's Top-K over the entries visible to it
                 bd.csa2_index_full(lb.q_idx, lb.w, k_idx, q_pos=self.q_pos, m=self.m,
-                                   scores=self.scores, stream=stream)
-                bd.csa2_topk(self.scores.view(self.Tq, self.N), self.K, valid_len=self.valid_len,
-                             out=self.sel[i].view(self.Tq, self.K), ws=self.ws, stream=stream)
+                                   scores=self.scores, K=self.K, sel=self.sel[i].view(self.Tq, self.K),
+                                   ws=self.ws, stream=stream)
             bd.csa2_sparse_attn(lb.q_main, codes, scales, self.selection_of(i), lb.swa,
                                 swa_scale=self.swa_scale, q_pos=self.q_pos, swa_pos0=self.swa_pos0,
-                                n_win=self.n_win, out=self.out[i], ws=self.ws, stream=stream)
+                                n_win=self.n_win, out=self.out[i], ws=self.attn_ws, stream=stream)
         return self.out

@@ -33,7 +33,10 @@ def test_workspace_queries_are_host_only():
     assert bd.csa2_topk_workspace(4, 4096, 512) == 0          # rows sorted whole in LDS
     assert bd.csa2_topk_workspace(8, 1 << 20, 512) > 8 * 8192 * 8
     assert bd.csa2_index_reindex_workspace(8, 16384, 512) >= 8 * 16384 * 4
-    assert bd.csa2_index_full_workspace(8, 1, 1 << 20, 128, 2048, 8) >= 8 * 8192 * 4
+    assert bd.csa2_index_full_workspace(8, 1, 1 << 20, 8, 128, 128, 2048, 8) >= 8 * 65536 * 4   # tile maxima
+    assert bd.csa2_index_full_workspace(8, 1, 1 << 20, 8, 128, 0, 0, 8, 0) == 0              # scores only
+    # a prefill-shaped call takes the row select (no candidate lists)
+    assert bd.csa2_index_full_workspace(1, 8192, 16384, 8, 128, 0, 0, 8, 512) < 1 << 20
     assert bd.csa2_sparse_attn_workspace(8192, 1, 64, 512, 512, 8319) == 0   # one split
     assert bd.csa2_sparse_attn_workspace(8, 1, 64, 512, 512, 128) > 0
 
@@ -65,7 +68,11 @@ def test_invalid_arguments_rejected_before_launch():
                               p, None, None, 0, None) == 2                      # H_q % 16
     assert L.csa2_topk(p, 1, 10, None, None, 4096, p, None, 0, None) == 2        # K > 2048
     assert L.csa2_index_full(p, p, p, 1, 1, 10, 6, 128, None, 1, p, None, None, 128, 2048, 8,
-                             None, 0, None) == 2                                 # h_i
+                             0, None, None, 0, None) == 2                        # h_i
+    assert L.csa2_index_full(p, p, p, 1, 1, 10, 8, 128, None, 1, p, None, None, 128, 2048, 8,
+                             4096, p, p, 1 << 30, None) == 2                     # K > 2048
+    assert L.csa2_index_full(p, p, p, 8, 1, 1 << 20, 8, 128, None, 1, p, None, None, 128, 2048, 8,
+                             512, p, p, 1024, None) == 3                         # workspace
     # workspace too small
     assert L.csa2_topk(p, 8, 1 << 20, None, None, 512, p, None, 0, None) == 3
     assert b"workspace" in L.csa2_last_error()

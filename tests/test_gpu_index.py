@@ -180,3 +180,61 @@ def test_reindex():
         pl = pool[b, :plen[b]]
         s = index_scores(q[b], w[b], k[b][pl])
         check_topk(sel[b], s, K, index_map=pl)
+
+
+@pytest.mark.parametrize("B,Tq,N,K,pool,kind", [
+    (2, 1, 300000, 512, True, "gauss"),    # pool and Top-K from the scan's tile maxima
+    (1, 1, 1 << 20, 512, True, "gauss"),   # a million entries: 8,192 blocks, 2,048 kept
+    (3, 1, 70001, 512, False, "gauss"),    # Top-K only, ragged row
+    (2, 1, 40000, 2048, True, "gauss"),    # K = 2,048: the threshold from 2,500 tiles
+    (1, 1, 20000, 2048, False, "gauss"),   # fewer tiles than K: every entry a candidate
+    (2, 1, 5000, 512, True, "gauss"),      # short rows: selected whole
+    (2, 1, 300000, 512, True, "ties"),     # integer scores: candidates overflow, exact fallback
+    (2, 3, 50000, 512, False, "gauss"),    # three queries per sequence at their own positions
+    (1, 1, 128 * 2048 + 77, 512, True, "gauss"),  # just over PB blocks, ragged last block
+])
+def test_full_layer_select(B, Tq, N, K, pool, kind):
+    """csa2_index_full with the pool and the layer's Top-K: both are functions of the
+    scores, so they must equal the oracle's pool and Top-K of the GPU's own scores
+    exactly, and the oracle's (from its float64 scores) under the near-tie rule."""
+    rng = np.random.default_rng(N + K + Tq)
+    h_i, d_i = 8, 128
+    if kind == "ties":   # small integers in bf16: exact products, scores on an integer grid
+        q = f64_to_bf16(rng.integers(-2, 3, (B, Tq, h_i, d_i)).astype(np.float64))
+        k = f64_to_bf16(rng.integers(-1, 2, (B, N, d_i)).astype(np.float64))
+        w = np.ones((B, Tq, h_i), np.float32)
+    else:
+        q = rand_bf16(rng, (B, Tq, h_i, d_i))
+        k = rand_bf16(rng, (B, N, d_i))
+        w = rng.random((B, Tq, h_i)).astype(np.float32)
+    qp = None
+    m = 1
+    if Tq > 1:
+        m = 2
+        qp = np.stack([np.arange(2 * N - 3000 * Tq, 2 * N, 3000, dtype=np.int32) for _ in range(B)])
+    res = bd().csa2_index_full(dev_bf16(q), dev(w), dev_bf16(k), q_pos=None if qp is None else dev(qp),
+                               m=m, with_pool=pool, K=K)
+    torch.cuda.synchronize()
+    if pool:
+        sc, gpool, plen, sel = res
+        gpool, plen = gpool.cpu().numpy(), plen.cpu().numpy()
+    else:
+        sc, sel = res
+    sc, sel = sc.cpu().numpy(), sel.cpu().numpy().reshape(B, Tq, K)
+    for b in range(B):
+        for t in range(Tq):
+            n = N if qp is None else visible_count(int(qp[b, t]), N, m)
+            g = sc[b, t].astype(np.float64)
+            ref = index_scores(q[b, t], w[b, t], k[b])
+            assert np.all(np.isneginf(g[n:]))
+            assert np.all(np.abs(g[:n] - ref[:n]) <= score_tol(q[b, t], w[b, t], k[b])[:n])
+            # exact on the GPU's scores, near-tie rule on the oracle's
+            assert check_topk(sel[b, t], g, K, n_vis=n, rel=0.0) == 0
+            check_topk(sel[b, t], ref, K, n_vis=n)
+            if pool:
+                r = b * Tq + t
+                want = build_pool(g, 128, 2048, 8, n_visible=n)
+                assert plen[r] == want.shape[0]
+                assert np.array_equal(gpool[r, :plen[r]], want)
+                assert np.all(gpool[r, plen[r]:] == -1)
+                check_pool(gpool[r, :plen[r]], ref, 128, 2048, 8, n_vis=n)
