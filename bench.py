@@ -7,8 +7,10 @@ layers, sparse attention in every layer), replayed from a captured HIP graph.
 Inputs (FP4 main KV, indexer keys, per-layer queries and windows) are built and
 resident in HBM before the timed region.
 
-Prints one JSON line.  Default workload: 64 sequences x 65,536 entries,
-[Full + Reuse x 3].
+Prints one JSON line.  Default workload: 8 sequences x 1,048,576 entries through
+the 20-layer decoder schedule (Full + Reuse x 3, then 4 x [Reindex + Reuse x 3]).
+Other workloads: --workload decode_64k_b64 | reindex_256k_b32 | mtp_64k_b64 |
+full_decode_4k | prefill_32k | append_b64.
 """
 from __future__ import annotations
 
@@ -34,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_64k_b64")
+    ap.add_argument("--workload", default="decode_1m_b8")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -45,6 +47,10 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size reference "
                          "for HBM byte counters)")
+    ap.add_argument("--profile-call", choices=["scan", "attn", "select"], default=None,
+                    help="decode workloads: after building the inputs, run only this call "
+                         "--kernel-reps times (the first layer's indexer scan, its attention, or "
+                         "the Full layer's pool + Top-K from its scores) and exit; for counter runs")
     return ap.parse_args()
 
 
@@ -93,6 +99,24 @@ def copy_calibration(args, torch):
     del src, dst
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=5) -> float:
+    """Measured device-to-device copy rate (read + write bytes / s, GB/s) of a plain
+    torch copy of `nbytes`: what this GPU's HBM delivers beside the 8 TB/s spec."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    return 2 * nbytes / t / 1e9
+
+
 def algorithmic_bytes(wl) -> dict:
     """Bytes a step must move at least: every Full layer streams the indexer keys
     of all entries; a Reindex layer gathers the keys of its pool; every layer reads
@@ -117,15 +141,38 @@ def build_inputs(wl, torch, bd, sch):
     kidx = torch.empty(B, N, wl.d_i, dtype=torch.bfloat16, device=dev)
     W = torch.from_numpy(synth.w_ik(wl).view(np.int16)).view(torch.bfloat16).to(dev)
     t0 = time.time()
-    workers = min(16, os.cpu_count() or 1)
-    with ThreadPoolExecutor(workers) as ex:
-        futs = [ex.submit(synth.main_kv, wl, b) for b in range(B)]
-        for b, f in enumerate(futs):
-            x = torch.from_numpy(f.result()).to(dev)
-            bd.csa2_quant_fp4(x, codes=codes[b], scales=scales[b], W_ik=W, k_idx=kidx[b])
-            del x
-    torch.cuda.synchronize()
-    log(f"cache built: {B} x {N} entries in {time.time() - t0:.1f}s")
+    build_us = None
+    if wl.T:
+        # the cache from hidden states: compressor (m tokens per entry) -> FP4 + keys
+        tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        H = tt(np.stack([synth.hidden(wl, b) for b in range(B)]))
+        Wkv, Wz = (tt(x) for x in synth.compressor_weights(wl))
+        kv = torch.empty(B, N, d, dtype=torch.float32, device=dev)
+        def build():
+            bd.csa2_compress(H, Wkv, Wz, wl.m, rope_dim=wl.rope_dim, out=kv)
+            bd.csa2_quant_fp4(kv.view(B * N, d), codes=codes.view(B * N, d // 2),
+                              scales=scales.view(B * N, d // 16), W_ik=W, k_idx=kidx.view(B * N, wl.d_i))
+        for _ in range(2):
+            build()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            build()
+        e1.record()
+        torch.cuda.synchronize()
+        build_us = e0.elapsed_time(e1) * 1e3 / 10
+        log(f"cache built from hidden states: {B} x {wl.T} tokens -> {N} entries, {build_us:.1f} us")
+    else:
+        workers = min(16, os.cpu_count() or 1)
+        with ThreadPoolExecutor(workers) as ex:
+            futs = [ex.submit(synth.main_kv, wl, b) for b in range(B)]
+            for b, f in enumerate(futs):
+                x = torch.from_numpy(f.result()).to(dev)
+                bd.csa2_quant_fp4(x, codes=codes[b], scales=scales[b], W_ik=W, k_idx=kidx[b])
+                del x
+        torch.cuda.synchronize()
+        log(f"cache built: {B} x {N} entries in {time.time() - t0:.1f}s")
     layers = []
     for li, mode in enumerate(wl.layers):
         qm = np.stack([synth.q_main(wl, li, b, wl.Tq) for b in range(B)])
@@ -138,7 +185,7 @@ def build_inputs(wl, torch, bd, sch):
         tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         layers.append(sch.LayerBuffers(tb(qm), tt(sw), None if qi is None else tb(qi),
                                        None if w is None else tt(w)))
-    return codes, scales, kidx, layers
+    return codes, scales, kidx, layers, build_us
 
 
 def time_scan(wl, torch, bd, kidx, layers, reps):
@@ -168,18 +215,35 @@ def oracle_threads() -> int:
         return 1
 
 
+# entries of the oracle's bounded sample of a decode workload (the oracle's setup
+# for a whole 1M-entry sequence alone -- quantiser and keys in float64 -- takes
+# over a minute of host time)
+CPU_SAMPLE_ENTRIES = 1 << 18
+
+
 def cpu_baseline(wl, seconds):
-    """The oracle, as it stands, on a bounded sample of the same workload: the
-    decode step of 2 sequences, repeated until `seconds` of CPU work."""
+    """The oracle, as it stands, on a bounded sample of the same workload: decode
+    steps of the first sequences (two, or one when the sample is shortened) through
+    the whole layer schedule, repeated until `seconds` of CPU work.  Sequences
+    longer than CPU_SAMPLE_ENTRIES entries are sampled as their first
+    CPU_SAMPLE_ENTRIES entries and the rate is scaled by the entry ratio (the scan
+    over all entries dominates a step), which the record states."""
     import synth
-    from oracle.csa2 import LayerInputs, decode_step, indexer_k, quant_fp4
+    from oracle.csa2 import LayerInputs, compress, decode_step, indexer_k, quant_fp4
     threads = oracle_threads()
     from oracle.csa2 import swa_window_rows
     W = synth.w_ik(wl)
+    n_e = min(wl.N, CPU_SAMPLE_ENTRIES)
+    nseq = 2 if n_e == wl.N else 1
     P, S = wl.N * wl.m, wl.S
     seqs = []
-    for b in range(2):
-        q8 = quant_fp4(synth.main_kv(wl, b))
+    for b in range(nseq):
+        if wl.T:   # the cache from hidden states, through the oracle's compressor
+            Wkv, Wz = synth.compressor_weights(wl)
+            kv = compress(synth.hidden(wl, b), Wkv, Wz, wl.m, rope_dim=wl.rope_dim).astype(np.float32)
+        else:
+            kv = synth.main_kv(wl, b, 0, n_e)
+        q8 = quant_fp4(kv)
         k = indexer_k(q8.codes, q8.scales, W)
         for t in range(wl.Tq):   # query t sees the window tokens up to its own position
             rows = (np.arange(S) if wl.Tq == 1 else
@@ -199,9 +263,20 @@ def cpu_baseline(wl, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n / el, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} single-query decode steps of sequences 0-1 of {wl.name} "
-                      f"({'+'.join(wl.layers)}, {wl.N} entries), {el:.1f}s, float64 numpy"}
+    rate = n / el
+    rec = {"value": rate * n_e / wl.N, "unit": "queries/s", "cores": int(threads),
+           "host_cpus": os.cpu_count(), "kind": "oracle"}
+    if n_e == wl.N:
+        rec["sample"] = (f"{n} single-query decode steps of sequences 0-{nseq - 1} of {wl.name} "
+                         f"({'+'.join(wl.layers)}, {wl.N} entries), {el:.1f}s, float64 numpy on "
+                         f"{threads} BLAS threads")
+    else:
+        rec["sample"] = (f"{n} single-query decode steps of sequence 0 of {wl.name} "
+                         f"({'+'.join(wl.layers)}) over its first {n_e} entries, {el:.1f}s, "
+                         f"float64 numpy on {threads} BLAS threads: {rate:.2f} steps/s, scaled by "
+                         f"{n_e}/{wl.N} entries")
+        rec["sample_rate"] = rate
+    return rec
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -260,7 +335,8 @@ def prefill_cpu_baseline(wl, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n / el, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+    return {"value": n / el, "unit": "tokens/s", "cores": oracle_threads(), "host_cpus": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{n} query rows (the last 64 of the chunk, cycled) through scores of every "
                       f"visible entry, Top-{wl.K} and attention in {len(wl.layers)} layers, {el:.1f}s, "
                       f"float64 numpy; the chunk's compressor, quantisation and keys ran untimed "
@@ -466,10 +542,38 @@ def append_main(args, wl, torch, bd):
             n += 1
         el = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": n * B / el, "unit": "tokens/s", "cores": oracle_threads(),
-                               "kind": "oracle",
+                               "host_cpus": os.cpu_count(), "kind": "oracle",
                                "sample": f"{n} appends of all {B} sequences (quantise, key, window), "
                                          f"{el:.1f}s, float64 numpy"}
     print(json.dumps(out), flush=True)
+
+
+def profile_call(args, wl, torch, bd, run, codes, scales, kidx, layers):
+    """One call of the first layer, --kernel-reps times, eagerly (for counter runs:
+    the kernels of that call are the only ones of the command besides setup)."""
+    lb = layers[0]
+    n = args.kernel_reps
+    if args.profile_call == "scan":
+        scores = torch.empty(wl.B, wl.Tq, wl.N, dtype=torch.float32, device="cuda")
+        fn = lambda: bd.csa2_index_full(lb.q_idx, lb.w, kidx, scores=scores)
+    elif args.profile_call == "select":
+        scores = torch.empty(wl.B, wl.Tq, wl.N, dtype=torch.float32, device="cuda")
+        pool = torch.empty(wl.B * wl.Tq, wl.PB * wl.PE, dtype=torch.int32, device="cuda")
+        plen = torch.empty(wl.B * wl.Tq, dtype=torch.int32, device="cuda")
+        sel = torch.empty(wl.B * wl.Tq, wl.K, dtype=torch.int32, device="cuda")
+        ws = torch.empty(bd.csa2_index_full_workspace(wl.B, wl.Tq, wl.N, wl.h_i, wl.d_i, wl.G, wl.PB,
+                                                      wl.PE, wl.K), dtype=torch.uint8, device="cuda")
+        fn = lambda: bd.csa2_index_full(lb.q_idx, lb.w, kidx, scores=scores, pool=pool, pool_len=plen,
+                                        K=wl.K, sel=sel, ws=ws)
+    else:
+        sel = torch.sort(torch.randint(0, wl.N, (wl.B, wl.Tq, wl.K), device="cuda"),
+                         dim=-1).values.to(torch.int32)
+        fn = lambda: bd.csa2_sparse_attn(lb.q_main, codes, scales, sel, lb.swa, out=run.out[0],
+                                         ws=run.attn_ws)
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    log(f"profile call {args.profile_call}: {n} calls on {wl.name}")
 
 
 def main():
@@ -493,13 +597,13 @@ def main():
         return prefill_main(args, wl, torch, bd, sch)
     if wl.append:
         return append_main(args, wl, torch, bd)
-    if wl.T:
-        raise SystemExit("workloads built from hidden states are parity cases, not bench lines")
     log(f"workload {wl.name}: B={wl.B} N={wl.N} d={wl.d} schedule={wl.schedule}")
-    codes, scales, kidx, layers = build_inputs(wl, torch, bd, sch)
+    codes, scales, kidx, layers, build_us = build_inputs(wl, torch, bd, sch)
     copy_calibration(args, torch)
     run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
                              G=wl.G, PB=wl.PB, PE=wl.PE, Tq=wl.Tq, full_in_pool=args.full_in_pool)
+    if args.profile_call:
+        return profile_call(args, wl, torch, bd, run, codes, scales, kidx, layers)
     step_kw = {}
     if wl.Tq > 1:   # the queries sit at positions P .. P+Tq-1; the window ends at the last
         P = wl.N * wl.m
@@ -533,6 +637,8 @@ def main():
     log(f"scan kernel: {scan_s * 1e6:.1f} us/launch, {achieved:.0f} GB/s")
 
     traffic = traffic_record(f"traffic_index_scores_{wl.name}.txt", "index.hip", "common.h")
+    copy_gbs = copy_bandwidth(torch)
+    log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
 
     out = {
         "metric": METRIC,
@@ -555,10 +661,14 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "index_scores_kernel (Full-layer indexer scan)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "launch_us": scan_s * 1e6, "algorithmic_bytes_per_launch": scan_bytes},
+                     "launch_us": scan_s * 1e6, "algorithmic_bytes_per_launch": scan_bytes,
+                     "measured_copy_GB_s": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "step_hbm": {"algorithmic_bytes": ab["total"], "GB_s": ab["total"] / step_s / 1e9,
                      "frac": ab["total"] / step_s / 1e9 / HBM_PEAK_GBS, "breakdown": ab},
     }
+    if wl.T:
+        out["config"].update({"tokens": wl.T, "d_model": wl.d_model, "hidden": "f32"})
+        out["cache_build_us"] = build_us
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

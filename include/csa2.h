@@ -255,6 +255,13 @@ CSA2_API int csa2_index_reindex(const void* q_idx, const float* w, const void* k
  *   ws     >= csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) bytes (0 when a row is
  *          not split over its keys)
  * Limits: d in {256, 512}, H_q % 16 == 0, K <= 2048.
+ * Kernels: up to 64 query rows (decode steps) with at most 512 selection slots,
+ * 128 visible window tokens, 0 < swa_scale <= 128 and 16-byte aligned q, out and
+ * caches, all keys of a row are handled inside one workgroup per (row, 16 heads,
+ * part of the dims), with no split partials and no merge launch (fp16 products,
+ * probabilities with 11 significant bits, queries scaled into fp16 by a power of
+ * two per head); the workspace is then unused.  Otherwise a split-K kernel and a
+ * merge launch.
  * Precision: products are exact (entries, window values and probabilities are
  * carried in fp16 or bf16, both exact for the decoded values) and accumulate in
  * fp32.  When H_q % 32 == 0, 0 < swa_scale <= 128 and codes, scales and swa are

@@ -38,6 +38,13 @@
 
 namespace csa2 {
 
+#ifndef CSA2_ROWS_MAX
+#define CSA2_ROWS_MAX 64  // query rows up to which the few-rows kernel runs (measured: faster up to 64)
+#endif
+#ifndef CSA2_ROWS_DP2_MAX
+#define CSA2_ROWS_DP2_MAX 128  // (row, 16-head group) units up to which it splits the output dims in two
+#endif
+
 #ifndef CSA2_ATTN_TARGET_WGS
 #define CSA2_ATTN_TARGET_WGS 256  // workgroups a launch aims for (splits = target / rows)
 #endif
@@ -435,6 +442,18 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
   const int rows = B * Tq;
   if (rows == 0) return hipSuccess;
   const int L_max = K + S;  // same bound as the workspace query
+  const float sm_log2_rows = sm_scale * 1.4426950408889634f;
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(scales) |
+                           reinterpret_cast<uintptr_t>(swa) | reinterpret_cast<uintptr_t>(q) |
+                           reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+  // Few rows (decode steps): every key of a row inside one workgroup per (row, 16
+  // heads, output-dim part), no split partials and no combine launch.
+  if (aligned16 && rows <= CSA2_ROWS_MAX &&
+      attn_rows_supported(H_q, d, K, S, n_win, q_pos != nullptr, swa_scale)) {
+    const int dp = rows * (H_q / 16) <= CSA2_ROWS_DP2_MAX ? 2 : 1;
+    return launch_sparse_attn_rows(q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
+                                   q_pos, Tq, H_q, d, sm_log2_rows, rows, dp, out, lse, st);
+  }
   const bool f16 = attn_f16_supported(H_q, d, swa_scale);
   AttnPlan p = attn_plan(B, Tq, H_q, K, L_max);
   // Rows so few that every split holds a single chunk: the fp16 kernel runs each

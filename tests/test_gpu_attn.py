@@ -2,8 +2,12 @@
 Bar: max |gpu - oracle| <= 2e-3 x RMS(oracle output) (fp32 accumulation); the
 log-sum-exp within 2e-4 x (1 + |oracle|).
 
-Shapes with H_q a multiple of 32 (and |swa_scale| <= 128) run the fp16 kernel,
-the others the bf16 kernel; both are covered here."""
+Three kernels serve the call, and each is covered here:
+* up to 64 query rows with at most 512 selection slots, 128 visible window tokens,
+  H_q a multiple of 16 and 0 < swa_scale <= 128: the few-rows kernel (a row's keys
+  in one workgroup, no split partials);
+* otherwise, H_q a multiple of 32 and 0 < swa_scale <= 128: the split-K fp16 kernel;
+* otherwise the split-K bf16 kernel."""
 import numpy as np
 import pytest
 import torch
@@ -118,3 +122,37 @@ def test_swa_scale_and_prefill_positions(swa_scale):
         compare(out[0, t], ref)
         compare_lse(lse[0, t], q[0, t], codes[0], scales[0], sel[0, t], swa[0], swa_scale,
                     q_pos=int(pos[0, t]), swa_pos0=swa_pos0, n_win=n_win)
+
+
+@pytest.mark.parametrize("H,K,n_sel,S", [
+    (64, 512, None, 128),    # split-K fp16 kernel (more than 128 rows)
+    (48, 512, None, 128),    # split-K bf16 kernel (H_q not a multiple of 32)
+    (64, 300, 77, 77),       # split-K fp16 kernel, ragged selection and window
+])
+def test_many_rows_split_kernels(H, K, n_sel, S):
+    """136 query rows (two sequences x 68 queries, more than the few-rows kernel
+    takes) run the split-K kernels; sampled rows against the oracle."""
+    rng = np.random.default_rng(H + K + S)
+    B, Tq, d, N = 2, 68, 512, 2000
+    codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S, n_sel)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device="cuda")
+    out = bd().csa2_sparse_attn(dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa),
+                                swa_scale=1.0, lse=lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b, t in [(0, 0), (0, 33), (1, 5), (1, 67)]:
+        ref = sparse_attention(q[b, t], codes[b], scales[b], sel[b, t], swa[b])
+        compare(out[b, t], ref)
+        compare_lse(lse[b, t], q[b, t], codes[b], scales[b], sel[b, t], swa[b])
+
+
+def test_few_rows_repeatable():
+    """8 rows x 64 heads take the few-rows kernel: calls on the same inputs give
+    bitwise identical outputs (every sum in a fixed order) that match the oracle."""
+    rng = np.random.default_rng(5)
+    B, H, d, N, K, S = 8, 64, 512, 3000, 512, 128
+    codes, scales, q, sel, swa = make_case(rng, B, 1, H, d, N, K, S)
+    args = (dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa))
+    outs = [bd().csa2_sparse_attn(*args).cpu().numpy() for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    for b in range(B):
+        compare(outs[0][b, 0], sparse_attention(q[b, 0], codes[b], scales[b], sel[b, 0], swa[b]))

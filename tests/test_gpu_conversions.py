@@ -12,7 +12,9 @@ that key as the kernel decoded it.  These tests make every decoded value visible
   swa_scale, exactly at swa_scale 1; at 0.37 the scale enters through the
   probability (a power of two split off in fp16 / a bf16 pair), so the bound is
   2^-10 relative, far below the 1/16 step between neighbouring E4M3 values;
-* both kernels: 32 heads (fp16 MFMA kernel) and 48 heads (bf16 kernel).
+* every kernel: up to 64 query rows the few-rows kernel (32 and 48 heads); with
+  136 rows (each query cycling over the entries / window tokens) the split-K
+  kernels, 32 heads (fp16) and 48 heads (bf16).
 """
 import numpy as np
 import pytest
@@ -49,30 +51,31 @@ def all_code_entries():
     return codes, scales
 
 
+@pytest.mark.parametrize("rows", [8, 136])
 @pytest.mark.parametrize("H_q", [32, 48])
-def test_every_fp4_code_under_every_scale(H_q):
+def test_every_fp4_code_under_every_scale(H_q, rows):
     codes, scales = all_code_entries()
     n = codes.shape[0]
     assert set(scales.reshape(-1).tolist()) == set(FINITE_E4M3.tolist())
     rng = np.random.default_rng(H_q)
-    q = f64_to_bf16(rng.standard_normal((1, n, H_q, D)))
-    sel = np.arange(n, dtype=np.int32).reshape(1, n, 1)            # query t selects entry t
-    swa = torch.empty(1, 0, D, dtype=torch.uint8, device="cuda")   # no window
+    q = f64_to_bf16(rng.standard_normal((1, rows, H_q, D)))
+    sel = (np.arange(rows, dtype=np.int32) % n).reshape(1, rows, 1)   # query t selects entry t mod n
+    swa = torch.empty(1, 0, D, dtype=torch.uint8, device="cuda")      # no window
     out = bd().csa2_sparse_attn(dev_bf16(q), dev(codes[None]), dev(scales[None]), dev(sel), swa)
     torch.cuda.synchronize()
-    out = out.cpu().numpy()[0]                                      # [n, H_q, D]
-    want = dequant_fp4(codes, scales)                                # exact, float64
+    out = out.cpu().numpy()[0]                                         # [rows, H_q, D]
+    want = dequant_fp4(codes, scales)                                   # exact, float64
     assert np.all(np.isfinite(want))
-    for t in range(n):
-        bad = np.nonzero(out[t] != want[t][None, :].astype(np.float32))
-        assert bad[0].size == 0, f"entry {t}: head {bad[0][0]}, channel {bad[1][0]}: " \
-                                 f"{out[t][bad[0][0], bad[1][0]]} vs {want[t][bad[1][0]]}"
+    for t in range(rows):
+        bad = np.nonzero(out[t] != want[t % n][None, :].astype(np.float32))
+        assert bad[0].size == 0, f"query {t}: head {bad[0][0]}, channel {bad[1][0]}: " \
+                                 f"{out[t][bad[0][0], bad[1][0]]} vs {want[t % n][bad[1][0]]}"
 
 
+@pytest.mark.parametrize("Tq", [4, 136])
 @pytest.mark.parametrize("H_q", [32, 48])
 @pytest.mark.parametrize("swa_scale", [1.0, 0.37])
-def test_every_fp8_window_code(H_q, swa_scale):
-    Tq = 4
+def test_every_fp8_window_code(H_q, swa_scale, Tq):
     tok = np.stack([FINITE_E4M3[(np.arange(D) + 37 * t) % FINITE_E4M3.shape[0]] for t in range(Tq)])
     assert set(tok[0].tolist()) == set(FINITE_E4M3.tolist())
     rng = np.random.default_rng(7 * H_q)

@@ -37,7 +37,7 @@ def test_decode_full_size_sampled(name, attn_layers):
     bench, bd, sch = mods()
     wl = synth.workload(name)
     print(f"[fullsize] {name}: B={wl.B} N={wl.N} schedule={wl.schedule}", flush=True)
-    codes, scales, kidx, layers = bench.build_inputs(wl, torch, bd, sch)
+    codes, scales, kidx, layers, _ = bench.build_inputs(wl, torch, bd, sch)
     run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
                              G=wl.G, PB=wl.PB, PE=wl.PE)
     g = run.capture(codes, scales, kidx, layers)
@@ -89,7 +89,7 @@ def test_multi_query_full_size_sampled():
     bench, bd, sch = mods()
     wl = synth.workload("mtp_64k_b64")
     print(f"[fullsize] {wl.name}: B={wl.B} N={wl.N} Tq={wl.Tq}", flush=True)
-    codes, scales, kidx, layers = bench.build_inputs(wl, torch, bd, sch)
+    codes, scales, kidx, layers, _ = bench.build_inputs(wl, torch, bd, sch)
     run = sch.DecodeSchedule(wl.layers, wl.B, wl.N, wl.d, wl.h_i, wl.d_i, wl.H_q, wl.S, wl.K,
                              Tq=wl.Tq)
     P = wl.N * wl.m
