@@ -41,6 +41,9 @@ namespace csa2 {
 #ifndef CSA2_ROWS_MAX
 #define CSA2_ROWS_MAX 64  // query rows up to which the few-rows kernel runs (measured: faster up to 64)
 #endif
+#ifndef CSA2_ROWS_DP4_MAX
+#define CSA2_ROWS_DP4_MAX 16  // rows up to which it splits the output dims in four (d = 512)
+#endif
 #ifndef CSA2_ROWS_DP2_MAX
 #define CSA2_ROWS_DP2_MAX 128  // (row, 16-head group) units up to which it splits the output dims in two
 #endif
@@ -450,7 +453,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
   // heads, output-dim part), no split partials and no combine launch.
   if (aligned16 && rows <= CSA2_ROWS_MAX &&
       attn_rows_supported(H_q, d, K, S, n_win, q_pos != nullptr, swa_scale)) {
-    const int dp = rows * (H_q / 16) <= CSA2_ROWS_DP2_MAX ? 2 : 1;
+    // output-dim parts: more workgroups (each with less to merge) when rows are few
+    const int dp = (rows <= CSA2_ROWS_DP4_MAX && d == 512) ? 4 : rows * (H_q / 16) <= CSA2_ROWS_DP2_MAX ? 2 : 1;
     return launch_sparse_attn_rows(q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
                                    q_pos, Tq, H_q, d, sm_log2_rows, rows, dp, out, lse, st);
   }

@@ -73,9 +73,9 @@ hipError_t launch_sparse_attn_f16(const uint16_t* q, const uint8_t* codes, const
                                   hipStream_t st);
 
 // few-rows kernel (attn_rows.hip): a row's keys inside one workgroup per (row,
-// 16 heads, output-dim part); dp = 1 or 2 parts.  Usable when H_q is a multiple of
-// 16, d is 256 or 512, at most 512 selection slots and 128 visible window tokens,
-// and 0 < swa_scale <= 128.
+// 16 heads, output-dim part); dp = 1, 2 or 4 parts (4 only for d = 512).  Usable
+// when H_q is a multiple of 16, d is 256 or 512, at most 512 selection slots and
+// 128 visible window tokens, and 0 < swa_scale <= 128.
 bool attn_rows_supported(int H_q, int d, int K, int S, int n_win, bool with_pos, float swa_scale);
 hipError_t launch_sparse_attn_rows(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                                    int N, const int* sel, int K, const uint8_t* swa, float swa_scale,

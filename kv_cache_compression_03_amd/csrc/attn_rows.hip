@@ -460,7 +460,8 @@ hipError_t launch_sparse_attn_rows(const uint16_t* q, const uint8_t* codes, cons
                      scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win, q_pos, Tq, H_q, sm_log2, \
                      rows, out, lse)
   if (d == 512) {
-    if (dp == 2) CSA2_ROWS(512, 2, 8);
+    if (dp == 4) CSA2_ROWS(512, 4, 8);
+    else if (dp == 2) CSA2_ROWS(512, 2, 8);
     else CSA2_ROWS(512, 1, 4);
   } else {
     if (dp == 2) CSA2_ROWS(256, 2, 8);
