@@ -164,7 +164,7 @@ CSA2_API int csa2_cache_append(const float* kv, int B, int d, long long cap, lon
  *   ws     >= csa2_index_full_workspace(B, Tq, N, h_i, d_i, G, PB, PE, K) bytes (pass
  *          G = 0 or PB = 0 without a pool, K = 0 without sel; 0 bytes when neither).
  * With a pool or sel, a decode-shaped call (up to 1,048,576 entries, G = 128 for
- * the pool) writes the maximum of every 16-entry tile beside the scores; the pool
+ * the pool) writes the maximum of every 32-entry span beside the scores; the pool
  * blocks and a provable lower bound of the K-th best score come from those
  * maxima, so only the pool blocks and the blocks that can hold a Top-K entry are
  * read again.
