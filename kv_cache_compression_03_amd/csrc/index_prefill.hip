@@ -116,8 +116,15 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(wv[n][u][i]));
     asm volatile("" : "+v"(nv[n]));
   }
+  int vmin = N;  // the fewest entries any of the wave's queries sees (rows past Tq: all N)
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o));
+  for (int n = 0; n < NG; ++n) vmin = min(vmin, wq0 + 4 * n + g < Tq ? nv[n] : N);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    vmax = max(vmax, __shfl_xor(vmax, o));
+    vmin = min(vmin, __shfl_xor(vmin, o));
+  }
+  vmin = __builtin_amdgcn_readfirstlane(vmin);
   if (lane == 0) s_vmax[wave] = vmax;
   // The workgroup's score rows as one raw buffer: a store whose offset falls
   // outside it is dropped by the hardware range check, so masked lanes (keys
@@ -169,20 +176,39 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the B operands of key tile ct+1 are read from LDS while the MFMAs of key tile
+    // ct run (the schedule below holds them in that order)
+    const uint16_t* kbase = &kt[buf][col * KP + 8 * g];
+    bf16x8_t kb[2][KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kb[0][s] = *reinterpret_cast<const bf16x8_t*>(kbase + 32 * s);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
+      if (ct + 1 < CT) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          kb[(ct + 1) & 1][s] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * (ct + 1) * KP + 32 * s);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][ct] = mfma16x16x32(qa[rt][s], kb[ct & 1][s], acc[rt][ct]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // LDS reads of key tile 0
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8_t kb =
-            *reinterpret_cast<const bf16x8_t*>(&kt[buf][(16 * ct + col) * KP + 32 * s + 8 * g]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt][ct] = mfma16x16x32(qa[rt][s], kb, acc[rt][ct]);
+        if (ct + 1 < CT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read ahead
+        __builtin_amdgcn_sched_group_barrier(0x008, RT, 0);                  // RT MFMAs
       }
-    }
-    // ---- epilogue: ReLU, head weights, head sum, causal mask (all within the lane)
+    // ---- epilogue: ReLU, head weights, head sum, causal mask (all within the lane);
+    // the stores follow the branch, so every path issues the same number of them
     const int key0 = key_lo + tile * kPfKeys;
+    float pv[NG][CT];
+    int of[NG][CT];
 #pragma unroll
-    for (int n = 0; n < NG; ++n) {
+    for (int n = 0; n < NG; ++n)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         float p = 0.0f;
@@ -190,11 +216,31 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
         for (int u = 0; u < TPG; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i) p = fmaf(wv[n][u][i], relu(acc[n * TPG + u][ct][i]), p);
-        const int j = key0 + 16 * ct + col;
-        const int off = j < N ? roff[n] + j * (int)sizeof(float) : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(j < nv[n] ? p : -INFINITY), srsc, off, 0, 0);
+        pv[n][ct] = p;
       }
+    if (key0 + kPfKeys <= vmin) {
+      // every key of the tile is visible to every query of the wave (and below N)
+#pragma unroll
+      for (int n = 0; n < NG; ++n) {
+        const int base = roff[n] + (key0 + col) * (int)sizeof(float);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) of[n][ct] = base + 64 * ct;
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NG; ++n)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int j = key0 + 16 * ct + col;
+          of[n][ct] = j < N ? roff[n] + j * (int)sizeof(float) : kOutOfRange;
+          if (j >= nv[n]) pv[n][ct] = -INFINITY;
+        }
     }
+#pragma unroll
+    for (int n = 0; n < NG; ++n)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pv[n][ct]), srsc, of[n][ct], 0, 0);
     __builtin_amdgcn_sched_barrier(0);  // stash after the stores
     // buffer buf^1 was last read in pass tile-1, before that pass's barrier
     CSA2_PF_STASH(buf ^ 1)
