@@ -17,7 +17,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
 
 SOURCES = ["api.cpp", "quant.hip", "compress.hip", "index.hip", "index_prefill.hip", "topk.hip",
-           "attn.hip", "attn_f16.hip", "attn_rows.hip"]
+           "attn.hip", "attn_f16.hip", "attn_rows.hip", "attn_wide.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -30,6 +30,13 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The many-rows attention kernel holds 128 output
+# accumulators per lane next to its query: without this the register allocator
+# parks the accumulators in AGPRs and copies them to VGPRs and back on every key
+# chunk (two VALU moves per element); with MFMA operands in VGPRs they stay put.
+EXTRA = {"attn_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -39,7 +46,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stderr or "").splitlines()
                      if "packed-fp32-ops" not in l)  # host pass does not know the feature

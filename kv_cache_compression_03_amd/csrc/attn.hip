@@ -44,6 +44,9 @@ namespace csa2 {
 #ifndef CSA2_ROWS_DP4_MAX
 #define CSA2_ROWS_DP4_MAX 16  // rows up to which it splits the output dims in four (d = 512)
 #endif
+#ifndef CSA2_WIDE_MIN_WGS
+#define CSA2_WIDE_MIN_WGS 1024  // (row, 64-head group) units from which the many-rows kernel runs
+#endif
 #ifndef CSA2_ROWS_DP2_MAX
 #define CSA2_ROWS_DP2_MAX 128  // (row, 16-head group) units up to which it splits the output dims in two
 #endif
@@ -458,6 +461,12 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
     return launch_sparse_attn_rows(q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
                                    q_pos, Tq, H_q, d, sm_log2_rows, rows, dp, out, lse, st);
   }
+  // Many rows (prefill chunks): a workgroup per (row, 64 heads), every logit and
+  // softmax term computed once, no split partials.
+  if (aligned16 && (long long)rows * (H_q / 64) >= CSA2_WIDE_MIN_WGS &&
+      attn_wide_supported(H_q, d, K, swa_scale))
+    return launch_sparse_attn_wide(q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
+                                   q_pos, Tq, H_q, d, sm_log2_rows, rows, out, lse, st);
   const bool f16 = attn_f16_supported(H_q, d, swa_scale);
   AttnPlan p = attn_plan(B, Tq, H_q, K, L_max);
   // Rows so few that every split holds a single chunk: the fp16 kernel runs each

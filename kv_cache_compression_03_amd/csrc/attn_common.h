@@ -1,4 +1,5 @@
-// Pieces shared by the two sparse-attention kernels (attn.hip, attn_f16.hip).
+// Pieces shared by the sparse-attention kernels (attn.hip, attn_f16.hip, attn_rows.hip,
+// attn_wide.hip).
 #pragma once
 
 #include "common.h"
@@ -82,5 +83,15 @@ hipError_t launch_sparse_attn_rows(const uint16_t* q, const uint8_t* codes, cons
                                    int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,
                                    int H_q, int d, float sm_log2, int rows, int dp, float* out,
                                    float* lse, hipStream_t st);
+
+// many-rows kernel (attn_wide.hip): a workgroup per (row, 64 heads), each wave 16
+// heads over all dims, no split partials.  Usable when H_q is a multiple of 64, d
+// is 256 or 512, at most 512 selection slots and 0 < swa_scale <= 128.
+bool attn_wide_supported(int H_q, int d, int K, float swa_scale);
+hipError_t launch_sparse_attn_wide(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                   int N, const int* sel, int K, const uint8_t* swa, float swa_scale,
+                                   int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,
+                                   int H_q, int d, float sm_log2, int rows, float* out, float* lse,
+                                   hipStream_t st);
 
 }  // namespace csa2

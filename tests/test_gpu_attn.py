@@ -2,10 +2,13 @@
 Bar: max |gpu - oracle| <= 2e-3 x RMS(oracle output) (fp32 accumulation); the
 log-sum-exp within 2e-4 x (1 + |oracle|).
 
-Three kernels serve the call, and each is covered here:
+Four kernels serve the call, and each is covered here:
 * up to 64 query rows with at most 512 selection slots, 128 visible window tokens,
   H_q a multiple of 16 and 0 < swa_scale <= 128: the few-rows kernel (a row's keys
   in one workgroup, no split partials);
+* at least 1024 (row, 64-head group) units, H_q a multiple of 64, at most 512
+  selection slots and 0 < swa_scale <= 128: the many-rows kernel (a workgroup per
+  row and 64 heads, no split partials);
 * otherwise, H_q a multiple of 32 and 0 < swa_scale <= 128: the split-K fp16 kernel;
 * otherwise the split-K bf16 kernel."""
 import numpy as np
@@ -156,3 +159,46 @@ def test_few_rows_repeatable():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     for b in range(B):
         compare(outs[0][b, 0], sparse_attention(q[b, 0], codes[b], scales[b], sel[b, 0], swa[b]))
+
+
+@pytest.mark.parametrize("H,d,K,n_sel,S,swa_scale,prefill", [
+    (64, 512, 512, None, 128, 1.0, False),   # prefill shape: 64 heads, d = 512
+    (64, 512, 300, 77, 77, 1.0, False),      # ragged selection and window
+    (128, 256, 512, None, 128, 1.0, False),  # d = 256, two 64-head groups per row
+    (64, 512, 512, None, 300, 0.37, True),   # window ring with positions, scaled window
+    (64, 512, 64, 0, 128, 100.0, False),     # empty selection: window only
+])
+def test_many_rows_wide_kernel(H, d, K, n_sel, S, swa_scale, prefill):
+    """1,040 query rows (two sequences x 520 queries) take the many-rows kernel;
+    sampled rows against the oracle, every row finite."""
+    rng = np.random.default_rng(H + d + K + S)
+    B, Tq, N = 2, 520, 2000
+    codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S, n_sel)
+    kw = {}
+    pos = None
+    if prefill:
+        swa_pos0, n_win = 1000, 128
+        pos = (1000 + np.arange(Tq, dtype=np.int32) * 7 // 13)[None].repeat(B, 0)  # window edges
+        kw = dict(q_pos=dev(pos), swa_pos0=swa_pos0, n_win=n_win)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device="cuda")
+    out = bd().csa2_sparse_attn(dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa),
+                                swa_scale=swa_scale, lse=lse, **kw)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for b, t in [(0, 0), (0, 1), (0, 257), (1, 130), (1, 519)]:
+        pk = {} if pos is None else dict(q_pos=int(pos[b, t]), swa_pos0=1000, n_win=128)
+        ref = sparse_attention(q[b, t], codes[b], scales[b], sel[b, t], swa[b], swa_scale, **pk)
+        compare(out[b, t], ref)
+        compare_lse(lse[b, t], q[b, t], codes[b], scales[b], sel[b, t], swa[b], swa_scale, **pk)
+
+
+def test_many_rows_wide_repeatable():
+    """The many-rows kernel sums in a fixed order: calls on the same inputs give
+    bitwise identical outputs."""
+    rng = np.random.default_rng(6)
+    B, Tq, H, d, N, K, S = 1, 1024, 64, 512, 3000, 512, 128
+    codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S)
+    args = (dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa))
+    outs = [bd().csa2_sparse_attn(*args).cpu().numpy() for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    compare(outs[0][0, 700], sparse_attention(q[0, 700], codes[0], scales[0], sel[0, 700], swa[0]))
