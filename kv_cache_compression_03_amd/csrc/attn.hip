@@ -464,7 +464,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
   // Many rows (prefill chunks): a workgroup per (row, 64 heads), every logit and
   // softmax term computed once, no split partials.
   if (aligned16 && (long long)rows * (H_q / 64) >= CSA2_WIDE_MIN_WGS &&
-      attn_wide_supported(H_q, d, K, swa_scale))
+      attn_wide_supported(H_q, d, K, N, S, swa_scale))
     return launch_sparse_attn_wide(q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
                                    q_pos, Tq, H_q, d, sm_log2_rows, rows, out, lse, st);
   const bool f16 = attn_f16_supported(H_q, d, swa_scale);

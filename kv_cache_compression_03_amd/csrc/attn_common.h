@@ -86,8 +86,9 @@ hipError_t launch_sparse_attn_rows(const uint16_t* q, const uint8_t* codes, cons
 
 // many-rows kernel (attn_wide.hip): a workgroup per (row, 64 heads), each wave 16
 // heads over all dims, no split partials.  Usable when H_q is a multiple of 64, d
-// is 256 or 512, at most 512 selection slots and 0 < swa_scale <= 128.
-bool attn_wide_supported(int H_q, int d, int K, float swa_scale);
+// is 256 or 512, at most 512 selection slots, 0 < swa_scale <= 128 and a sequence's
+// codes (N x d/2 bytes) and window (S x d bytes) each below 2 GiB.
+bool attn_wide_supported(int H_q, int d, int K, int N, int S, float swa_scale);
 hipError_t launch_sparse_attn_wide(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                                    int N, const int* sel, int K, const uint8_t* swa, float swa_scale,
                                    int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,

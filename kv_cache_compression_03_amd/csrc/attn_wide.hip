@@ -131,20 +131,26 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
   // kinds arrive through the same NLD 16-byte loads into the same registers
   const int dkey = tid & 31, dseg = tid >> 5;
   wu4_t raw[NLD];
+  // raw buffers over this row's sequence (32-bit offsets; the launch checks the
+  // extents fit)
+  const __amdgpu_buffer_rsrc_t r_codes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes) + (size_t)b * N * (D / 2), (short)0, N * (D / 2), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t r_scales = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(scales) + (size_t)b * N * (D / 16), (short)0, N * (D / 16), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t r_swa = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(swa) + (size_t)b * S * D, (short)0, S * D, kRawBufferWord3);
   auto load_raw = [&](int c) {
     const bool mc = c < nm;
     const int e = mc ? max(s_ent[c * kKC + dkey], 0) : 0;  // padding reads entry 0, masked later
-    const size_t ent = (size_t)b * N + e;
-    const uint8_t* cb = codes + ent * (D / 2) + ((dseg * (VPT / 2)) & ~15);
-    const uint8_t* sb = scales + ent * (D / 16) + ((dseg * NSB) & ~15);
     const int t = (c - nm) * kKC + dkey;
-    const uint8_t* wb =
-        swa + ((size_t)b * S + window_slot(win, t >= 0 && t < n_swa ? t : 0, S)) * D + dseg * VPT;
+    const int wo = window_slot(win, t >= 0 && t < n_swa ? t : 0, S) * D + dseg * VPT;
+    const int co = e * (D / 2) + ((dseg * (VPT / 2)) & ~15);
+    const int so = e * (D / 16) + ((dseg * NSB) & ~15);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const uint8_t* m = i < NCL ? cb + 16 * i : sb;
-      const uint8_t* w = i < NWL ? wb + 16 * i : wb;
-      raw[i] = *reinterpret_cast<const wu4_t*>(mc ? m : w);
+      const __amdgpu_buffer_rsrc_t r = mc ? (i < NCL ? r_codes : r_scales) : r_swa;
+      const int off = mc ? (i < NCL ? co + 16 * i : so) : (i < NWL ? wo + 16 * i : wo);
+      raw[i] = __builtin_bit_cast(wu4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
   };
   // ---- decode the raw registers into one LDS buffer (exact fp16)
@@ -300,8 +306,15 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
         // the logit is rounded on its own (as the reference maximum is), so the
         // lazy bound below holds for the value exponentiated
         asm("" : "+v"(x));
-        lg[4 * t + i] = ((vmask >> (16 * t + 4 * g + i)) & 1u) ? x : -INFINITY;
+        lg[4 * t + i] = x;
       }
+    }
+    if (vmask != 0xFFFFFFFFu) {  // a chunk with masked keys (most have none)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((vmask >> (16 * t + 4 * g + i)) & 1u)) lg[4 * t + i] = -INFINITY;
     }
     float lmax = lg[0];
 #pragma unroll
@@ -393,9 +406,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
 
 }  // namespace
 
-bool attn_wide_supported(int H_q, int d, int K, float swa_scale) {
+bool attn_wide_supported(int H_q, int d, int K, int N, int S, float swa_scale) {
+  // a sequence's codes and window must be addressable by 32-bit buffer offsets
   return H_q % kWideHeads == 0 && (d == 256 || d == 512) && K <= kWideMaxSel && swa_scale > 0.0f &&
-         swa_scale <= 128.0f;
+         swa_scale <= 128.0f && (long long)N * (d / 2) < (1ll << 31) && (long long)S * d < (1ll << 31);
 }
 
 hipError_t launch_sparse_attn_wide(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,

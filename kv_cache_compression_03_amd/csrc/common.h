@@ -10,6 +10,10 @@
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
+// Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format); a buffer
+// access whose offset falls outside the descriptor's range reads zero / is dropped.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // ---------------------------------------------------------------- bf16
 
 CSA2_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

@@ -26,7 +26,6 @@ namespace csa2 {
 constexpr int kPfWaves = 4;
 constexpr int kPfRows = 256;  // (query, head) rows per workgroup, 64 per wave
 constexpr int kPfKeys = 64;   // keys per staged tile
-constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family: 32-bit data)
 constexpr int kOutOfRange = 0x7FFFFFF0;      // a byte offset past any score buffer of this kernel
 #ifndef CSA2_PF_SPLIT
 #define CSA2_PF_SPLIT 4096    // keys per workgroup
