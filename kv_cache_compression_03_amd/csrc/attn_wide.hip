@@ -22,10 +22,10 @@
 //   * S^T = K·Q^T on MFMA 16x16x32 f16: two 16-key tiles; A = keys read from LDS
 //     (16 bytes per lane), B = the wave's fp16 query half in registers;
 //   * lazy online softmax in the S^T layout (lane = one head, 8 keys);
-//   * O += P·V on MFMA 16x16x16 f16 over the wave's D/32 output tiles, one 16-key
-//     tile per MFMA: the 4 probabilities a lane holds for a tile are exactly its A
-//     operand, and V comes from the same LDS rows through the transposing read
-//     (ds_read_b64_tr_b16).
+//   * O += P·V on MFMA 16x16x32 f16 over the wave's D/32 output tiles: the 8
+//     probabilities a lane holds (4 keys of each tile) are exactly its A operand,
+//     and V comes from the same LDS rows through two transposing reads
+//     (ds_read_b64_tr_b16), one per key tile.
 // LDS layout of a chunk: key r at byte r(2D+32) + 16[r >= 16].  A 16-byte LDS
 // access by a wave is served per 32-lane half and is conflict-free when each half
 // hits distinct 4-byte banks out of 128 (measured): with a row stride of 32 mod 512
@@ -58,10 +58,6 @@ constexpr int kPrefV = 4;          // V read pairs issued ahead of their MFMA
 // column l%16 in element i.
 CSA2_DEV wf4_t mfma16x16x32_f16(w8_t a, w8_t b, wf4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-// D(16x16, f32) += A(16x16, f16) * B(16x16, f16); reduction elements 4(l/16) .. +3.
-CSA2_DEV wf4_t mfma16x16x16_f16(w4_t a, w4_t b, wf4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 // 8 bytes per lane from LDS, transposed inside each 16-lane group: lane j of the
 // group receives element j%4 of what lanes 4e + j/4 (e = 0..3) addressed.
@@ -342,33 +338,33 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
     // sum gains the rounded values divided by ks.  While no key has been seen
     // (m_ref = -inf) every lg is -inf and p = 0.
     const float mp = m_ref == -INFINITY ? 0.0f : m_ref - (main_chunk ? 0.0f : log2_swa);
-    w4_t pa[2];
+    w8_t pa;  // A operand of P·V: reduction slots 8g .. 8g+7 = keys 4g .. 4g+3 of each tile
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pa[t][i] = (_Float16)__builtin_amdgcn_exp2f(lg[4 * t + i] - mp);
+    for (int k = 0; k < 8; ++k) pa[k] = (_Float16)__builtin_amdgcn_exp2f(lg[k] - mp);
     // the row sum adds the rounded probabilities (exact products in the dot)
     float psum = 0.0f;
     const w2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa[t], pa[t], 0, 1), one2, psum, false);
-      psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa[t], pa[t], 2, 3), one2, psum, false);
-    }
+    psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 0, 1), one2, psum, false);
+    psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 2, 3), one2, psum, false);
+    psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 4, 5), one2, psum, false);
+    psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 6, 7), one2, psum, false);
     l_run += main_chunk ? psum : psum * inv_swa;
-    // ---- O += P·V over the wave's output tiles, one 16-key tile per MFMA
+    // ---- O += P·V over the wave's output tiles: one 16x16x32 MFMA per tile over
+    // both key tiles (a 16x16x16 MFMA occupies the matrix unit as long as a
+    // 16x16x32 one, so the wider reduction halves the matrix time)
     {
       const uint8_t* vb = buf_c + pv_off;
 #pragma unroll
       for (int n = 0; n < NO; ++n) {
-        o[n] = mfma16x16x16_f16(pa[0], lds_read_tr(vb + 32 * n), o[n]);
-        o[n] = mfma16x16x16_f16(pa[1], lds_read_tr(vb + T1 + 32 * n), o[n]);
+        const w4_t lo = lds_read_tr(vb + 32 * n);
+        const w4_t hi = lds_read_tr(vb + T1 + 32 * n);
+        o[n] = mfma16x16x32_f16(pa, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), o[n]);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPrefV, 0);
 #pragma unroll
-      for (int n = 0; n < 2 * NO; ++n) {
+      for (int n = 0; n < NO; ++n) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (n + 2 * kPrefV < 2 * NO) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (n + kPrefV < NO) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
     // ---- decode chunk c+2 into the buffer chunk c-1 used (last read in step c-1),
