@@ -137,14 +137,20 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
   for (int n = 0; n < NG; ++n) roff[n] = (wq0 - qb0 + 4 * n + g) * N * (int)sizeof(float);
 
   // staging of key tile `tile`: thread tid moves 16-byte chunks tid + u*256
-  // (key c / CPK, dims (c % CPK)*8 ..) through registers into LDS
+  // (key c / CPK, dims (c % CPK)*8 ..) through registers into LDS.  The keys are
+  // read through a buffer descriptor over the sequence's keys: the per-thread byte
+  // offset is fixed, the tile's offset is one uniform value, and keys past N read
+  // as zeros (their scores are masked).
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   u32x4 stg[CPT];
+  const __amdgpu_buffer_rsrc_t krsc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(k_idx) + (size_t)b * N * DI, (short)0, N * DI * (int)sizeof(uint16_t), kRawBufferWord3);
 #define CSA2_PF_FETCH(tile_)                                                                   \
   _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                            \
     const int c = tid + u * (kPfWaves * 64);                                                   \
-    const int j = min(key_lo + (tile_) * kPfKeys + c / CPK, N - 1);                            \
-    stg[u] = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)b * N + j) * DI + (c % CPK) * 8); \
+    stg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(                  \
+        krsc, ((c / CPK) * DI + (c % CPK) * 8) * (int)sizeof(uint16_t),                        \
+        (key_lo + (tile_) * kPfKeys) * DI * (int)sizeof(uint16_t), 0));                        \
   }
 #define CSA2_PF_STASH(buf_)                                                                    \
   _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                            \
@@ -261,9 +267,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
 }
 
 bool index_prefill_supported(int Tq, int N, int h_i, int d_i, const int* gather) {
-  // a workgroup's score rows (at most 64 of N floats) must fit one raw buffer below kOutOfRange
+  // a workgroup's score rows (at most 64 of N floats) must fit one raw buffer below
+  // kOutOfRange, and a sequence's keys one buffer descriptor
   return gather == nullptr && (long long)Tq * h_i >= kPfRows && (h_i == 4 || h_i == 8 || h_i == 16) &&
-         (d_i == 64 || d_i == 128) && (long long)(kPfRows / 4) * N * sizeof(float) < kOutOfRange;
+         (d_i == 64 || d_i == 128) && (long long)(kPfRows / 4) * N * sizeof(float) < kOutOfRange &&
+         (long long)N * d_i * 2 < (1ll << 31);
 }
 
 hipError_t launch_index_prefill(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
