@@ -29,8 +29,8 @@ constexpr int kScanWaves = 4;
 constexpr int kScanBatch = CSA2_SCAN_BATCH;  // entry tiles whose keys are in flight together
 static_assert(kScanBatch * 16 == kTmaxSpan, "one score maximum per batch of tiles");
 
-// QG query tiles per wave (several queries per sequence, e.g. drafted positions):
-// each key tile is loaded once and multiplied by all of them.
+// QG query tiles per wave; the launcher uses it with QG = 1 (one query tile per
+// sequence row group) and index_scores_mq_kernel below for more.
 // TM: also write the maximum of every 16-entry tile of each score row.
 template <int HI, int DI, int QG, bool TM>
 __global__ __launch_bounds__(kScanWaves * 64, QG == 1 ? 7 : 1) void index_scores_kernel(
@@ -153,6 +153,189 @@ __global__ __launch_bounds__(kScanWaves * 64, QG == 1 ? 7 : 1) void index_scores
   }
 }
 
+// Waves per SIMD the register budget is sized for (every variant without scratch).
+constexpr int scan_occupancy(int HI, int QG, bool TM) {
+  return !TM ? (QG == 2 ? 7 : 6) : (QG == 2 ? 5 : (HI == 4 ? 4 : 5));
+}
+
+// Several query tiles per wave (QG >= 2: several queries per sequence, e.g.
+// drafted positions): each key tile is loaded once and multiplied by all of them.
+// The A operands (and head weights) are the same for every wave of the workgroup,
+// so they are staged once in LDS instead of each wave holding QG tiles of them in
+// registers: more waves fit per SIMD, so more key loads are in flight.  All loads
+// are issued from clamped addresses and masked after (no load behind a branch),
+// and the first batch's key loads go out before the staging barrier.
+// TM: also write the maximum of every 32-entry span of each score row.
+template <int HI, int DI, int QG, bool TM>
+__global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void index_scores_mq_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, const int* __restrict__ gather,
+    const int* __restrict__ gather_len, const int* __restrict__ q_pos, int m, int Tq, int N, int L,
+    int tiles_per_wave, float* __restrict__ scores, float* __restrict__ tmax) {
+  constexpr int QPT = 16 / HI;     // queries per A tile
+  constexpr int KS = DI / 32;      // MFMA reduction steps
+  static_assert(QG >= 2, "one query tile takes index_scores_kernel");
+  constexpr bool QL = true;  // A operands staged in LDS (lane-indexed, 16 bytes per lane and step)
+  __shared__ __attribute__((aligned(16))) uint4 s_qa[QL ? QG * KS * 64 : 1];
+  __shared__ __attribute__((aligned(16))) float4 s_w[QL ? QG * 64 : 1];  // head weights per lane
+  // the wave index is uniform: keep it (and the entry range) in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int b = blockIdx.z;
+  const int tw0 = blockIdx.y * QG * QPT;   // first query of this workgroup
+
+  // A operand of query tile qg, step s for lane l: row l%16 of the tile (query
+  // t0 + row/HI, head row%HI), reduction slots of group l/16 (16 bytes)
+  // (loads are issued unconditionally from a clamped row and masked after, so the
+  // staging loads of a thread are all in flight together)
+  auto load_qa = [&](int qg, int s, int l) {
+    const int t = tw0 + qg * QPT + (l & 15) / HI, h = (l & 15) % HI;
+    const uint4 v =
+        reinterpret_cast<const uint4*>(q_idx + (((size_t)b * Tq + min(t, Tq - 1)) * HI + h) * DI)[s * 4 + (l >> 4)];
+    return t < Tq ? v : make_uint4(0, 0, 0, 0);
+  };
+  bf16x8_t qa[QL ? 1 : QG][KS];
+  if constexpr (QL) {
+    constexpr int NQ = (QG * KS * 64 + kScanWaves * 64 - 1) / (kScanWaves * 64);
+    uint4 qv[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int i = min((int)threadIdx.x + j * kScanWaves * 64, QG * KS * 64 - 1);
+      qv[j] = load_qa(i / (KS * 64), (i / 64) % KS, i % 64);
+    }
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int i = threadIdx.x + j * kScanWaves * 64;
+      if (i < QG * KS * 64) s_qa[i] = qv[j];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[0][s] = as_bf16x8(load_qa(0, s, lane));
+  }
+  // ---- head weights (lane l, element i: row 4(l/16) + i of the tile), visibility
+  // and output rows, kept for the whole range (the weights in LDS with the queries
+  // when there are several query tiles)
+  auto load_w = [&](int qg, int l) {
+    float4 v;
+    float* vp = reinterpret_cast<float*>(&v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * (l >> 4) + i, t = tw0 + qg * QPT + r / HI;
+      const float x = w[((size_t)b * Tq + min(t, Tq - 1)) * HI + (r % HI)];
+      vp[i] = t < Tq ? x : 0.0f;
+    }
+    return v;
+  };
+  float4 wr[QL ? 1 : QG];
+  if constexpr (QL) {
+    constexpr int NW = (QG * 64 + kScanWaves * 64 - 1) / (kScanWaves * 64);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int i = threadIdx.x + j * kScanWaves * 64;
+      const float4 v = load_w(min(i, QG * 64 - 1) / 64, i % 64);
+      if (i < QG * 64) s_w[i] = v;
+    }
+  } else {
+    wr[0] = load_w(0, lane);
+  }
+  int nvis_row[QG];   // entries visible to this lane's query (decode: all)
+  bool writer[QG];
+  const int myq0 = tw0 + (4 * g) / HI;  // this lane's query in tile 0; tile qg adds qg*QPT
+  float* const srow0 = scores + ((size_t)b * Tq + myq0) * L;
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const int myq = myq0 + qg * QPT;
+    nvis_row[qg] = L;
+    if (q_pos != nullptr && myq < Tq) {
+      long long p = q_pos[(size_t)b * Tq + myq];
+      long long nv = (p + 1) / m;
+      nvis_row[qg] = (int)(nv < 0 ? 0 : (nv > L ? L : nv));
+    }
+    writer[qg] = (g % (HI / 4 >= 1 ? HI / 4 : 1)) == 0 && myq < Tq;
+  }
+  int Lb = L;
+  if (gather_len != nullptr) Lb = min(L, gather_len[b]);
+
+  const long long wave_first = ((long long)blockIdx.x * kScanWaves + wave) * tiles_per_wave * 16;
+  const uint16_t* kb = k_idx + (size_t)b * N * DI;
+  const int* gb = gather ? gather + (size_t)b * L : nullptr;
+
+  for (int tile = 0; tile < tiles_per_wave; tile += kScanBatch) {
+    uint4 kv[kScanBatch][KS];
+    int ent[kScanBatch];
+    bool ent_ok[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const long long e = wave_first + (long long)(tile + u) * 16 + col;
+      ent[u] = (int)e;
+      bool live = (tile + u) < tiles_per_wave && e < Lb;
+      long long row = e;
+      if (gb) {  // uniform: the gathered row of every slot is read, masked after
+        row = gb[min(e, (long long)L - 1)];
+        live = live && row >= 0 && row < N;  // an entry outside the cache scores -inf
+      }
+      ent_ok[u] = live;
+      // dead entries read row 0 (their scores are masked): the same loads on every path
+      const uint4* kr = reinterpret_cast<const uint4*>(kb + (size_t)(live ? row : 0) * DI);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kv[u][s] = kr[s * 4 + g];
+    }
+    // the staged queries are complete once every wave has passed here; the first
+    // batch's key loads are already in flight (the trip count is the same for all)
+    if constexpr (QL) {
+      if (tile == 0) __syncthreads();
+    }
+    // TM: the maximum of the batch's 32 entries for each query row goes out per
+    // query tile (the 16 columns of a query are one 16-lane row of the wave)
+    const int nmt = (L + kTmaxSpan - 1) / kTmaxSpan;
+    const int mt = (int)((wave_first + (long long)tile * 16) / kTmaxSpan);
+    // the staged A operands are re-read every batch (an opaque index keeps the
+    // compiler from hoisting all of them into registers)
+    int qli = lane;
+    asm volatile("" : "+v"(qli));
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      // both tiles of the batch against query tile qg: each A operand read once
+      f32x4_t acc[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8_t a = QL ? as_bf16x8(s_qa[(qg * KS + s) * 64 + qli]) : qa[0][s];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) acc[u] = mfma16x16x32(a, as_bf16x8(kv[u][s]), acc[u]);
+      }
+      const float4 wq = QL ? s_w[qg * 64 + qli] : wr[0];
+      const float wv[4] = {wq.x, wq.y, wq.z, wq.w};
+      float bm = -INFINITY;  // TM: this lane's maximum over the batch's tiles
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (tile + u >= tiles_per_wave) break;
+        const int e = ent[u];
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wv[i], fmaxf(acc[u][i], 0.0f), v);
+        if (HI >= 8) v += __shfl_xor(v, 16);
+        if (HI >= 16) v += __shfl_xor(v, 32);
+        const float sv = (ent_ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
+        if (writer[qg] && e < L) srow0[(size_t)qg * QPT * L + e] = sv;
+        if constexpr (TM) bm = fmaxf(bm, e < L ? sv : -INFINITY);
+      }
+      if constexpr (TM) {
+        const float tv = row16_max(bm);
+        // query row qi of the tile sits in lane row qi * HI / 4: its maximum is taken
+        // to a scalar and stored by lane 0 (uniform addresses, few vector registers)
+#pragma unroll
+        for (int qi = 0; qi < QPT; ++qi) {
+          const int t = tw0 + qg * QPT + qi;
+          const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), 16 * qi * (HI / 4 >= 1 ? HI / 4 : 1)));
+          if (lane == 0 && t < Tq && mt < nmt) tmax[((size_t)b * Tq + t) * nmt + mt] = v;
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                                const int* gather, const int* gather_len, const int* q_pos, int m,
                                int B, int Tq, int N, int L, int h_i, int d_i, float* scores,
@@ -173,21 +356,21 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   tpw = (tpw + kScanBatch - 1) / kScanBatch * kScanBatch;
   const long long bx = (tiles + (long long)tpw * kScanWaves - 1) / ((long long)tpw * kScanWaves);
   dim3 grid((unsigned)bx, (unsigned)qgroups, (unsigned)B), block(kScanWaves * 64);
-#define CSA2_SCAN_Q(HI_, DI_, QG_)                                                                     \
+#define CSA2_SCAN_K(KERN_, HI_, DI_, QG_)                                                                \
   do {                                                                                                  \
     if (tmax)                                                                                           \
-      hipLaunchKernelGGL((index_scores_kernel<HI_, DI_, QG_, true>), grid, block, 0, st, q_idx, w, k_idx, \
-                         gather, gather_len, q_pos, m, Tq, N, L, tpw, scores, tmax);                    \
+      hipLaunchKernelGGL((KERN_<HI_, DI_, QG_, true>), grid, block, 0, st, q_idx, w, k_idx, gather,    \
+                         gather_len, q_pos, m, Tq, N, L, tpw, scores, tmax);                            \
     else                                                                                                \
-      hipLaunchKernelGGL((index_scores_kernel<HI_, DI_, QG_, false>), grid, block, 0, st, q_idx, w,     \
-                         k_idx, gather, gather_len, q_pos, m, Tq, N, L, tpw, scores, tmax);             \
+      hipLaunchKernelGGL((KERN_<HI_, DI_, QG_, false>), grid, block, 0, st, q_idx, w, k_idx, gather,   \
+                         gather_len, q_pos, m, Tq, N, L, tpw, scores, tmax);                            \
   } while (0)
-#define CSA2_SCAN(HI_, DI_)                     \
-  do {                                          \
-    if (qg == 1) CSA2_SCAN_Q(HI_, DI_, 1);      \
-    else if (qg == 2) CSA2_SCAN_Q(HI_, DI_, 2); \
-    else if (qg == 3) CSA2_SCAN_Q(HI_, DI_, 3); \
-    else CSA2_SCAN_Q(HI_, DI_, 4);              \
+#define CSA2_SCAN(HI_, DI_)                                           \
+  do {                                                                \
+    if (qg == 1) CSA2_SCAN_K(index_scores_kernel, HI_, DI_, 1);       \
+    else if (qg == 2) CSA2_SCAN_K(index_scores_mq_kernel, HI_, DI_, 2); \
+    else if (qg == 3) CSA2_SCAN_K(index_scores_mq_kernel, HI_, DI_, 3); \
+    else CSA2_SCAN_K(index_scores_mq_kernel, HI_, DI_, 4);            \
   } while (0)
   if (h_i == 8 && d_i == 128) CSA2_SCAN(8, 128);
   else if (h_i == 8 && d_i == 64) CSA2_SCAN(8, 64);
@@ -196,7 +379,7 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   else if (h_i == 16 && d_i == 128) CSA2_SCAN(16, 128);
   else CSA2_SCAN(16, 64);
 #undef CSA2_SCAN
-#undef CSA2_SCAN_Q
+#undef CSA2_SCAN_K
   return hipGetLastError();
 }
 
