@@ -8,30 +8,32 @@
 // the whole dequantised entry, shared by all query heads; one softmax over all
 // keys; window tokens are E4M3 values times swa_scale.
 //
-// Work split: a workgroup owns one query row and 64 heads, in eight waves, two per
-// SIMD.  Wave w = (head tile w%4, half h = w/4) owns heads 16(w%4) .. +15 and the
-// dims [hD/2, (h+1)D/2): it holds its heads' query over those dims, computes the
-// partial S^T of a chunk's 32 keys over them and swaps the partial tiles with its
-// partner (the other half of the head tile) through LDS; both then hold the same
-// logits, run the same softmax (bitwise equal) and accumulate O for their own
-// half of the output dims, so no partial outputs are merged.
+// Work split: a workgroup owns one query row and 64 heads in four waves; two
+// workgroups share a CU (one wave of each per SIMD, so their barriers and phases
+// are independent).  Wave w owns heads 16w .. 16w+15 over all D dims: its query
+// (B operand of S^T, fp16) and its output accumulators stay in registers, so no
+// partial logits are exchanged and every softmax is computed once.
 // The row's keys pass in 32-key chunks (selected entries first, then window
-// tokens), each decoded once, exactly to fp16, into a key-major LDS buffer by all
-// 512 threads.  Three buffers and one barrier per step: step c decodes chunk c+2,
-// forms the partial logits of chunk c+1 and finishes chunk c.
+// tokens), each decoded once, exactly to fp16, into a key-major LDS buffer.  Two
+// buffers and one barrier per step: step c attends chunk c while chunk c+1 is
+// decoded into the other buffer.  Raw chunk bytes never occupy registers across a
+// step: wave w stages the bytes of keys 8w .. 8w+7 (one half of the dims at a
+// time) through its own 2 KB of LDS with 16-byte loads that write LDS directly,
+// and decodes what it staged, so no other wave touches its staging.  The first
+// half of chunk c+1 is decoded between the softmax and P·V of chunk c (loaded at
+// the end of step c-1), the second half after P·V (loaded before it).
 //   * S^T = K·Q^T on MFMA 16x16x32 f16: two 16-key tiles; A = keys read from LDS
-//     (16 bytes per lane), B = the wave's fp16 query half in registers;
+//     (16 bytes per lane), B = the wave's fp16 query in registers;
 //   * lazy online softmax in the S^T layout (lane = one head, 8 keys);
-//   * O += P·V on MFMA 16x16x32 f16 over the wave's D/32 output tiles: the 8
+//   * O += P·V on MFMA 16x16x32 f16 over the D/16 output tiles: the 8
 //     probabilities a lane holds (4 keys of each tile) are exactly its A operand,
 //     and V comes from the same LDS rows through two transposing reads
 //     (ds_read_b64_tr_b16), one per key tile.
 // LDS layout of a chunk: key r at byte r(2D+32) + 16[r >= 16].  A 16-byte LDS
 // access by a wave is served per 32-lane half and is conflict-free when each half
 // hits distinct 4-byte banks out of 128 (measured): with a row stride of 32 mod 512
-// bytes the K reads (16 keys x two 16-byte columns per half) are, the transposing
-// V reads (8 keys x 32 bytes per half) are, and the 16-byte shift of the second
-// tile keeps the decode writes (32 keys, one column) apart as well.
+// bytes the K reads (16 keys x two 16-byte columns per half) are, and so are the
+// transposing V reads (8 keys x 32 bytes per half).
 // The bf16 query is moved into fp16 exactly by a power of two per head (the
 // head's largest |q| lands in [2^14, 2^15)), which is undone on the logits.
 // Probabilities are rounded to fp16 once and the row sums add the rounded values.
@@ -47,9 +49,9 @@ typedef float wf4_t __attribute__((ext_vector_type(4)));
 typedef short ws4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t wu4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWideThreads = 512;  // eight waves: 4 head tiles x 2 key halves
+constexpr int kWideThreads = 256;  // four waves of 16 heads
 constexpr int kWideHeads = 64;     // heads per workgroup, 16 per wave
-constexpr int kWideMaxSel = 512;   // selection slots the kernel takes (staged in LDS)
+constexpr int kWideMaxSel = 512;   // selection slots the kernel takes (held in LDS)
 constexpr int kPrefK = 6;          // K reads issued ahead of their MFMA
 constexpr int kPrefV = 4;          // V read pairs issued ahead of their MFMA
 
@@ -76,38 +78,36 @@ CSA2_DEV w2_t e4m3_pair(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
 }
 
+// a value the compiler must treat as unknown where it is used (keeps lane-derived
+// values from being hoisted out of the loop into registers that stay live)
+CSA2_DEV int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// The kernel body takes its LDS arrays as restrict pointers: the compiler then knows
+// that the chunk buffers never alias the staging that 16-byte loads write straight
+// into LDS, and waits for those loads only where the staged bytes are read.
 template <int D>
-__global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
+__device__ __attribute__((always_inline)) void sparse_attn_wide_body(
+    uint8_t* __restrict__ kv, uint8_t* __restrict__ stg_all, int* __restrict__ s_ent,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, int N, const int* __restrict__ sel, int K,
     const uint8_t* __restrict__ swa, float swa_scale, int S, long long swa_pos0, int n_win,
     const int* __restrict__ q_pos, int Tq, int H_q, float sm_log2, int rows, int head_groups,
     float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int NS = D / 64;                   // S^T MFMA steps per tile (half the dims)
-  constexpr int NO = D / 32;                   // output tiles of 16 dims in the wave's half
+  constexpr int NS = D / 32;                   // S^T MFMA steps per key tile (all dims)
+  constexpr int NO = D / 16;                   // output tiles of 16 dims
   constexpr int KSTB = 2 * D + 32;             // bytes per key row in LDS (second tile + 16)
   constexpr int KBUF = kKC * KSTB + 16;        // bytes per chunk buffer
-  constexpr int VPT = kKC * D / kWideThreads;  // values each thread decodes per chunk
-  constexpr int NU = VPT / 8;                  // 16-byte LDS units each thread writes
-  constexpr int NCL = VPT >= 32 ? VPT / 32 : 1;  // 16-byte code loads of a selected entry
-  constexpr int NSB = VPT / 16;                // its E4M3 block scales
-  constexpr int NWL = VPT / 16;                // 16-byte loads of a window token
-  constexpr int NLD = NCL + 1 > NWL ? NCL + 1 : NWL;
-  static_assert((VPT == 16 || VPT == 32) && KSTB % 512 == 32, "decode split");
-  // LDS: three chunk buffers, the exchanged partial tiles (parity, head tile, half,
-  // key tile: 64 lanes x 16 bytes each)
-  constexpr int KV_BYTES = 3 * KBUF;
-  __shared__ __attribute__((aligned(16))) uint8_t kv[KV_BYTES];
-  __shared__ __attribute__((aligned(16))) wf4_t xch[2][4][2][2][64];
-  __shared__ int s_ent[kWideMaxSel];
+  static_assert(KSTB % 512 == 32, "LDS row stride");
 
   int row, hgrp;
   if (!xcd_map(blockIdx.x, rows, head_groups, row, hgrp)) return;
   const int b = row / Tq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ht = wave & 3, kh = wave >> 2;  // head tile; half of the dims
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hc = lane & 15, g = lane >> 4;  // MFMA row / column and lane group
-  const int head0 = hgrp * kWideHeads + ht * 16;
+  const int head0 = hgrp * kWideHeads + wave * 16;
 
   // selection slots (ascending, -1 padded) rounded up to whole chunks; slots that
   // are not a valid entry are masked
@@ -123,10 +123,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
   const int n_chunks = nm + (n_swa + kKC - 1) / kKC;
   __syncthreads();
 
-  // ---- raw bytes of a chunk: thread = (key dkey, dims [dseg*VPT, +VPT)); both
-  // kinds arrive through the same NLD 16-byte loads into the same registers
-  const int dkey = tid & 31, dseg = tid >> 5;
-  wu4_t raw[NLD];
+  // ---- chunk bytes are staged per wave: wave w loads and decodes keys 8w .. 8w+7
+  // of every chunk, one half of the dims at a time, through its own 2 KB of LDS
+  // (16-byte loads straight into LDS: lane l's bytes land at base + 16 l)
+  constexpr int CU = D / 64;   // 16-byte code units per key and half
+  constexpr int WU = D / 32;   // 16-byte window units per key and half
+  constexpr int VPL = D / 16;  // values each lane decodes per half
+  constexpr int NWI = (8 * WU + 63) / 64;  // load instructions of a window half
+  static_assert(8 * CU <= 64 && 16 * 8 * CU <= 1024 && 16 * 8 * WU <= 2048, "staging split");
+  uint8_t* const my_stg = stg_all + 2048 * wave;
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
   // raw buffers over this row's sequence (32-bit offsets; the launch checks the
   // extents fit)
   const __amdgpu_buffer_rsrc_t r_codes = __builtin_amdgcn_make_buffer_rsrc(
@@ -135,35 +141,59 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
       const_cast<uint8_t*>(scales) + (size_t)b * N * (D / 16), (short)0, N * (D / 16), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t r_swa = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(swa) + (size_t)b * S * D, (short)0, S * D, kRawBufferWord3);
-  auto load_raw = [&](int c) {
-    const bool mc = c < nm;
-    const int e = mc ? max(s_ent[c * kKC + dkey], 0) : 0;  // padding reads entry 0, masked later
-    const int t = (c - nm) * kKC + dkey;
-    const int wo = window_slot(win, t >= 0 && t < n_swa ? t : 0, S) * D + dseg * VPT;
-    const int co = e * (D / 2) + ((dseg * (VPT / 2)) & ~15);
-    const int so = e * (D / 16) + ((dseg * NSB) & ~15);
+  // issue the loads of half h of chunk c (the wave's eight keys) into its staging:
+  // codes of key k at 16 CU k, its block scales at 1024 + 16 k; window bytes of key
+  // k at 16 WU k.  Padding slots read entry 0 / the first window token (masked).
+  auto stage = [&](int c, int h) {
+    const int ln = opaque(lane);
+    if (c < nm) {
+      if (ln < 8 * CU) {
+        const int e = max(s_ent[c * kKC + 8 * wave + ln / CU], 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_codes, (lds_ptr_t)my_stg, 16,
+                                                 e * (D / 2) + (D / 4) * h + 16 * (ln % CU), 0, 0, 0);
+      }
+      if (ln < 8) {
+        const int e = max(s_ent[c * kKC + 8 * wave + ln], 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_scales, (lds_ptr_t)(my_stg + 1024), 16,
+                                                 e * (D / 16) + (D / 32) * h, 0, 0, 0);
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const __amdgpu_buffer_rsrc_t r = mc ? (i < NCL ? r_codes : r_scales) : r_swa;
-      const int off = mc ? (i < NCL ? co + 16 * i : so) : (i < NWL ? wo + 16 * i : wo);
-      raw[i] = __builtin_bit_cast(wu4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+      for (int i = 0; i < NWI; ++i) {
+        const int u = 64 * i + ln, k = u / WU;
+        const int t = (c - nm) * kKC + 8 * wave + k;
+        const int slot = window_slot(win, t < n_swa ? t : 0, S);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_swa, (lds_ptr_t)(my_stg + 1024 * i), 16,
+                                                 slot * D + (D / 2) * h + 16 * (u % WU), 0, 0, 0);
+      }
     }
   };
-  // ---- decode the raw registers into one LDS buffer (exact fp16)
-  auto decode = [&](uint8_t* buf, bool main_chunk) {
-    uint8_t* rp = buf + dkey * KSTB + (dkey & 16) + dseg * (2 * VPT);
+  // the wave's staged loads have landed in LDS / its staging reads have returned
+  auto wait_staged = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  auto wait_lds = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  // ---- decode half h of the staged chunk into an LDS buffer (exact fp16): lane =
+  // (key k = l % 8, dims D/2 h + VPL (l / 8) .. +VPL-1)
+  auto decode_half = [&](uint8_t* buf, bool main_chunk, int h) {
+    const int ln = opaque(lane), k = ln & 7, seg = ln >> 3;
+    const int r = 8 * wave + k;
+    uint8_t* rp = buf + r * KSTB + (r & 16) + (D / 2 * h + VPL * seg) * 2;
     if (main_chunk) {
-      const int so = (dseg * NSB) & 15;  // this thread's scale bytes inside the 16-byte block
-      const wu4_t sv = raw[NCL];
-      const uint32_t sw = ((so >> 2) == 0 ? sv[0] : (so >> 2) == 1 ? sv[1] : (so >> 2) == 2 ? sv[2] : sv[3]) >>
-                          (8 * (so & 3));
+      uint32_t cw[VPL / 8];  // 8 codes per word
+      if constexpr (VPL == 32) {
+        const wu4_t v = *reinterpret_cast<const wu4_t*>(my_stg + 16 * CU * k + 16 * seg);
+        cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(my_stg + 16 * CU * k + 8 * seg);
+        cw[0] = v.x; cw[1] = v.y;
+      }
+      const uint8_t* sp = my_stg + 1024 + 16 * k + (VPL / 16) * seg;
+      const uint32_t sw = VPL == 32 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : (uint32_t)*sp;
       const w2_t s01 = e4m3_pair<false>(sw);
       const w2_t mm[2] = {w2_t{s01[0], s01[0]}, w2_t{s01[1], s01[1]}};
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        // codes of dims 8u .. 8u+7 of the range (VPT = 16: half dseg%2 of the block)
-        const uint32_t w = VPT >= 32 ? raw[u / 4][u % 4] : raw[0][2 * (dseg & 1) + u];
-        const w2_t sc = mm[u / 2];  // their block scale
+      for (int u = 0; u < VPL / 8; ++u) {
+        const uint32_t w = cw[u];
+        const w2_t sc = mm[u / 2];  // dims 8u .. 8u+7 share the block scale u/2
         const wu4_t pk = {__builtin_bit_cast(uint32_t, e2m1_pair<0>(w) * sc),
                           __builtin_bit_cast(uint32_t, e2m1_pair<1>(w) * sc),
                           __builtin_bit_cast(uint32_t, e2m1_pair<2>(w) * sc),
@@ -171,43 +201,43 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
         *reinterpret_cast<wu4_t*>(rp + 16 * u) = pk;
       }
     } else {
+      const uint8_t* wp = my_stg + 16 * WU * k + VPL * seg;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const uint32_t w0 = raw[u / 2][2 * (u % 2)], w1 = raw[u / 2][2 * (u % 2) + 1];
-        const wu4_t pk = {__builtin_bit_cast(uint32_t, e4m3_pair<false>(w0)),
-                          __builtin_bit_cast(uint32_t, e4m3_pair<true>(w0)),
-                          __builtin_bit_cast(uint32_t, e4m3_pair<false>(w1)),
-                          __builtin_bit_cast(uint32_t, e4m3_pair<true>(w1))};
-        *reinterpret_cast<wu4_t*>(rp + 16 * u) = pk;
+      for (int j = 0; j < VPL / 16; ++j) {
+        const wu4_t v = *reinterpret_cast<const wu4_t*>(wp + 16 * j);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t w0 = v[2 * q], w1 = v[2 * q + 1];
+          const wu4_t pk = {__builtin_bit_cast(uint32_t, e4m3_pair<false>(w0)),
+                            __builtin_bit_cast(uint32_t, e4m3_pair<true>(w0)),
+                            __builtin_bit_cast(uint32_t, e4m3_pair<false>(w1)),
+                            __builtin_bit_cast(uint32_t, e4m3_pair<true>(w1))};
+          *reinterpret_cast<wu4_t*>(rp + 32 * j + 16 * q) = pk;
+        }
       }
     }
   };
-  // chunk c sits in buffer c mod 3; the three buffer addresses rotate each step (a
+  // chunk c sits in buffer c mod 2; the two buffer addresses swap each step (a
   // plain base per step lets every read take its offset as an immediate)
-  uint8_t* buf_c = kv;                       // chunk c
-  uint8_t* buf_n = kv + KBUF;                // chunk c+1
-  uint8_t* buf_d = kv + 2 * KBUF;            // chunk c+2 (being decoded)
+  uint8_t* buf_c = kv;         // chunk c (attended)
+  uint8_t* buf_n = kv + KBUF;  // chunk c+1 (being decoded)
 
-  if (n_chunks > 0) load_raw(0);
-
-  // ---- the wave's query half (B operand of S^T): lane (head hc, group g) holds
-  // dims D/2*kh + 32s + 8g .. +7, moved into fp16 by the head's power of two (from
-  // the head's largest |q| over all dims, so both halves use the same one)
+  // ---- the wave's query (B operand of S^T): lane (head hc, group g) holds dims
+  // 32s + 8g .. +7, moved into fp16 by the head's power of two
   w8_t qh[NS];
   float qs;  // logits of head hc = S^T * qs
   {
     const uint16_t* qr = q + ((size_t)row * H_q + head0 + hc) * D + 8 * g;
     float mx = 0.0f;
-    wu4_t mineq[NS];
+    wu4_t qr4[NS];
 #pragma unroll
-    for (int s = 0; s < 2 * NS; ++s) {
-      const wu4_t r = *reinterpret_cast<const wu4_t*>(qr + 32 * s);
+    for (int s = 0; s < NS; ++s) {
+      qr4[s] = *reinterpret_cast<const wu4_t*>(qr + 32 * s);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        mx = fmaxf(mx, fabsf(__uint_as_float(r[k] << 16)));
-        mx = fmaxf(mx, fabsf(__uint_as_float(r[k] & 0xFFFF0000u)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(qr4[s][k] << 16)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(qr4[s][k] & 0xFFFF0000u)));
       }
-      if (s / NS == kh) mineq[s % NS] = r;
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -219,76 +249,66 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        qh[s][2 * k] = (_Float16)(__uint_as_float(mineq[s][k] << 16) * inv);
-        qh[s][2 * k + 1] = (_Float16)(__uint_as_float(mineq[s][k] & 0xFFFF0000u) * inv);
+        qh[s][2 * k] = (_Float16)(__uint_as_float(qr4[s][k] << 16) * inv);
+        qh[s][2 * k + 1] = (_Float16)(__uint_as_float(qr4[s][k] & 0xFFFF0000u) * inv);
       }
     }
   }
 
-  // S^T A operand: MFMA row hc of tile t = key 16t + hc, dims D/2*kh + 32s + 8g
-  const int qk_off = hc * KSTB + kh * D + 16 * g;
-  constexpr int T1 = 16 * KSTB + 16;  // offset of key tile 1
-  // partial S^T of chunk c's two tiles over this wave's dims, published for the partner
-  auto partial = [&](const uint8_t* buf, int c, wf4_t (&pt)[2]) {
-    const uint8_t* kb = buf + qk_off;
-    pt[0] = pt[1] = wf4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const w8_t ka = *reinterpret_cast<const w8_t*>(kb + t * T1 + 64 * s);
-        pt[t] = mfma16x16x32_f16(ka, qh[s], pt[t]);
-      }
-    }
-    // schedule: the first reads well ahead, then one read per MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, kPrefK, 0);
-#pragma unroll
-    for (int k = 0; k < 2 * NS; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (k + kPrefK < 2 * NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    xch[c & 1][ht][kh][0][lane] = pt[0];
-    xch[c & 1][ht][kh][1][lane] = pt[1];
-  };
-
-  // ---- prologue: chunks 0 and 1 decoded, chunk 2 in flight, partials of chunk 0
-  // published
-  wf4_t mine[2] = {wf4_t{0.f, 0.f, 0.f, 0.f}, wf4_t{0.f, 0.f, 0.f, 0.f}};
+  // ---- prologue: chunk 0 decoded, the first half of chunk 1 in flight
   if (n_chunks > 0) {
-    decode(buf_c, 0 < nm);
+    stage(0, 0);
+    wait_staged();
+    decode_half(buf_c, 0 < nm, 0);
+    wait_lds();
+    stage(0, 1);
+    wait_staged();
+    decode_half(buf_c, 0 < nm, 1);
     if (1 < n_chunks) {
-      load_raw(1);
-      decode(buf_n, 1 < nm);
-      if (2 < n_chunks) load_raw(2);
+      wait_lds();
+      stage(1, 0);
     }
-    lds_barrier();
-    partial(buf_c, 0, mine);
   }
   lds_barrier();
+
+  // S^T A operand: MFMA row hc of tile t = key 16t + hc, dims 32s + 8g .. +7
+  const int qk_off = hc * KSTB + 16 * g;
+  constexpr int T1 = 16 * KSTB + 16;  // offset of key tile 1
+  // transposing V read of tile t: lane 4e + q of group g addresses key 16t + 4g + e,
+  // dims 16n + 4q .. +3; it receives dim 16n + hc of the keys of S^T rows
+  // 4g .. 4g+3 (its P elements)
+  const int pv_off = (4 * g + ((lane & 15) >> 2)) * KSTB + 8 * (lane & 3);
 
   wf4_t o[NO];
 #pragma unroll
   for (int n = 0; n < NO; ++n) o[n] = wf4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.0f;
   const float log2_swa = log2f(swa_scale), inv_swa = 1.0f / swa_scale;  // swa_scale > 0 here
-  // transposing V read of tile t: lane 4e + q of group g addresses key 16t + 4g + e,
-  // dims D/2*kh + 16n + 4q .. +3; it receives dim D/2*kh + 16n + hc of the keys of
-  // S^T rows 4g .. 4g+3 (its P elements)
-  const int pv_off = (4 * g + ((lane & 15) >> 2)) * KSTB + kh * D + 8 * (lane & 3);
 
   for (int c = 0; c < n_chunks; ++c) {
     const bool main_chunk = c < nm;
-    // ---- logits of chunk c: the two halves' partial tiles added in dim order
-    wf4_t st[2];
+    // ---- S^T of chunk c over all dims: two 16-key tiles
+    wf4_t st[2] = {wf4_t{0.f, 0.f, 0.f, 0.f}, wf4_t{0.f, 0.f, 0.f, 0.f}};
+    {
+      const uint8_t* kb = buf_c + qk_off;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const wf4_t other = xch[c & 1][ht][kh ^ 1][t][lane];
-      st[t] = kh ? other + mine[t] : mine[t] + other;
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const w8_t ka = *reinterpret_cast<const w8_t*>(kb + t * T1 + 64 * s);
+          st[t] = mfma16x16x32_f16(ka, qh[s], st[t]);
+        }
+      }
+      // schedule: the first reads well ahead, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, kPrefK, 0);
+#pragma unroll
+      for (int k = 0; k < 2 * NS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (k + kPrefK < 2 * NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
-    // ---- partial logits of chunk c+1 (decoded in step c-1)
-    if (c + 1 < n_chunks) partial(buf_n, c + 1, mine);
     // ---- validity of the chunk's 32 keys (bit r = key r)
-    const int kr = lane & 31;
+    const int kr = opaque(lane) & 31;
     const bool ok = main_chunk ? s_ent[c * kKC + kr] >= 0 : (c - nm) * kKC + kr < n_swa;
     const uint32_t vmask = (uint32_t)__ballot(ok);
     const float ks = main_chunk ? 1.0f : swa_scale;
@@ -306,11 +326,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
       }
     }
     if (vmask != 0xFFFFFFFFu) {  // a chunk with masked keys (most have none)
+      // lane-derived values are formed here, not kept in registers over the loop
+      const uint32_t vm = vmask >> opaque(4 * g);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!((vmask >> (16 * t + 4 * g + i)) & 1u)) lg[4 * t + i] = -INFINITY;
+          if (!((vm >> (16 * t + i)) & 1u)) lg[4 * t + i] = -INFINITY;
     }
     float lmax = lg[0];
 #pragma unroll
@@ -319,15 +341,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
     // 2^kLazy; the head's four lanes then agree on the new value.
     const bool up_lane = lmax > m_ref + kLazy || (m_ref == -INFINITY && lmax != -INFINITY);
     if (__ballot(up_lane)) {
-      float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const int ln = opaque(lane);  // shuffle addresses are formed here (rarely taken)
+      float cmax = fmaxf(lmax, __shfl(lmax, ln ^ 16));
+      cmax = fmaxf(cmax, __shfl(cmax, ln ^ 32));
       const bool up = cmax > m_ref + kLazy || (m_ref == -INFINITY && cmax != -INFINITY);
       const float alpha = up ? (m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - cmax)) : 1.0f;
       m_ref = up ? cmax : m_ref;
       l_run *= alpha;
       float al[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * (ln >> 4) + i);
 #pragma unroll
       for (int n = 0; n < NO; ++n) {
 #pragma unroll
@@ -349,9 +372,16 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
     psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 4, 5), one2, psum, false);
     psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 6, 7), one2, psum, false);
     l_run += main_chunk ? psum : psum * inv_swa;
-    // ---- O += P·V over the wave's output tiles: one 16x16x32 MFMA per tile over
-    // both key tiles (a 16x16x16 MFMA occupies the matrix unit as long as a
-    // 16x16x32 one, so the wider reduction halves the matrix time)
+    // ---- first half of chunk c+1: decode what was staged, stage the second half
+    if (c + 1 < n_chunks) {
+      wait_staged();
+      decode_half(buf_n, c + 1 < nm, 0);
+      wait_lds();
+      stage(c + 1, 1);
+    }
+    // ---- O += P·V over the output tiles: one 16x16x32 MFMA per tile over both
+    // key tiles (a 16x16x16 MFMA occupies the matrix unit as long as a 16x16x32
+    // one, so the wider reduction halves the matrix time)
     {
       const uint8_t* vb = buf_c + pv_off;
 #pragma unroll
@@ -367,20 +397,23 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
         if (n + kPrefV < NO) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
-    // ---- decode chunk c+2 into the buffer chunk c-1 used (last read in step c-1),
-    // load chunk c+3
-    if (c + 2 < n_chunks) {
-      decode(buf_d, c + 2 < nm);
-      if (c + 3 < n_chunks) load_raw(c + 3);
+    // ---- second half of chunk c+1 (its buffer was last read in step c-1); the
+    // first half of chunk c+2 goes out
+    if (c + 1 < n_chunks) {
+      wait_staged();
+      decode_half(buf_n, c + 1 < nm, 1);
+      if (c + 2 < n_chunks) {
+        wait_lds();
+        stage(c + 2, 0);
+      }
     }
     uint8_t* const t = buf_c;
     buf_c = buf_n;
-    buf_n = buf_d;
-    buf_d = t;
+    buf_n = t;
     lds_barrier();
   }
 
-  // ---- epilogue: O element i of lane l is head 4g + i, dim D/2*kh + 16n + hc
+  // ---- epilogue: O element i of lane l is head 4g + i, dim 16n + hc
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   float rl[4];
@@ -389,15 +422,31 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_attn_wide_kernel(
     const float v = __shfl(l_tot, 4 * g + i);
     rl[i] = v > 0.0f ? 1.0f / v : 0.0f;
   }
-  float* orow = out + ((size_t)row * H_q + head0) * D + kh * (D / 2) + hc;
+  float* orow = out + ((size_t)row * H_q + head0) * D + hc;
 #pragma unroll
   for (int n = 0; n < NO; ++n) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) orow[(size_t)(4 * g + i) * D + 16 * n] = o[n][i] * rl[i];
   }
-  if (lse != nullptr && kh == 0 && g == 0)
+  if (lse != nullptr && g == 0)
     lse[(size_t)row * H_q + head0 + hc] =
         l_tot > 0.0f ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWideThreads, 2) void sparse_attn_wide_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, int N, const int* __restrict__ sel, int K,
+    const uint8_t* __restrict__ swa, float swa_scale, int S, long long swa_pos0, int n_win,
+    const int* __restrict__ q_pos, int Tq, int H_q, float sm_log2, int rows, int head_groups,
+    float* __restrict__ out, float* __restrict__ lse) {
+  // LDS: two chunk buffers (the chunk being attended, the next being decoded), the
+  // waves' staging of raw chunk bytes, the row's selection
+  __shared__ __attribute__((aligned(16))) uint8_t kv[2 * (kKC * (2 * D + 32) + 16)];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[kWideThreads / 64 * 2048];
+  __shared__ int s_ent[kWideMaxSel];
+  sparse_attn_wide_body<D>(kv, stg, s_ent, q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
+                           q_pos, Tq, H_q, sm_log2, rows, head_groups, out, lse);
 }
 
 }  // namespace
