@@ -54,6 +54,7 @@ constexpr int kWideHeads = 64;     // heads per workgroup, 16 per wave
 constexpr int kWideMaxSel = 512;   // selection slots the kernel takes (held in LDS)
 constexpr int kPrefK = 6;          // K reads issued ahead of their MFMA
 constexpr int kPrefV = 4;          // V read pairs issued ahead of their MFMA
+constexpr int kStageBytes = 3072;  // LDS staging of raw chunk bytes per wave
 
 // D(16x16, f32) += A(16x32, f16) * B(32x16, f16); lane l holds A row l%16 / B
 // column l%16 with reduction elements 8(l/16) .. +7, and D rows 4(l/16)+i,
@@ -99,7 +100,7 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
   constexpr int NS = D / 32;                   // S^T MFMA steps per key tile (all dims)
   constexpr int NO = D / 16;                   // output tiles of 16 dims
   constexpr int KSTB = 2 * D + 32;             // bytes per key row in LDS (second tile + 16)
-  constexpr int KBUF = kKC * KSTB + 16;        // bytes per chunk buffer
+  constexpr int KBUF = kKC * KSTB;             // bytes per chunk buffer (row 31's shift fits its padding)
   static_assert(KSTB % 512 == 32, "LDS row stride");
 
   int row, hgrp;
@@ -124,14 +125,20 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
   __syncthreads();
 
   // ---- chunk bytes are staged per wave: wave w loads and decodes keys 8w .. 8w+7
-  // of every chunk, one half of the dims at a time, through its own 2 KB of LDS
-  // (16-byte loads straight into LDS: lane l's bytes land at base + 16 l)
-  constexpr int CU = D / 64;   // 16-byte code units per key and half
+  // of every chunk through its own 3 KB of LDS (16-byte loads that write LDS
+  // directly: lane l's bytes land at base + 16 l).  A chunk of selected entries is
+  // staged whole (codes of key k at k D/2, its block scales at 4 D + k D/16); a
+  // window chunk one half of the dims at a time (key k's bytes at k D/2).
+  constexpr int CUK = D / 32;  // 16-byte code units per key
+  constexpr int SUK = D / 256; // 16-byte scale units per key
   constexpr int WU = D / 32;   // 16-byte window units per key and half
   constexpr int VPL = D / 16;  // values each lane decodes per half
+  constexpr int SOFF = 4 * D;  // staged scales after the wave's 8 keys of codes
+  constexpr int NCI = 8 * CUK / 64;        // load instructions of a chunk's codes
   constexpr int NWI = (8 * WU + 63) / 64;  // load instructions of a window half
-  static_assert(8 * CU <= 64 && 16 * 8 * CU <= 1024 && 16 * 8 * WU <= 2048, "staging split");
-  uint8_t* const my_stg = stg_all + 2048 * wave;
+  static_assert(8 * CUK % 64 == 0 && 8 * SUK <= 64 && SOFF + 8 * 16 * SUK <= kStageBytes &&
+                    16 * 8 * WU <= kStageBytes, "staging split");
+  uint8_t* const my_stg = stg_all + kStageBytes * wave;
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   // raw buffers over this row's sequence (32-bit offsets; the launch checks the
   // extents fit)
@@ -141,32 +148,41 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
       const_cast<uint8_t*>(scales) + (size_t)b * N * (D / 16), (short)0, N * (D / 16), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t r_swa = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(swa) + (size_t)b * S * D, (short)0, S * D, kRawBufferWord3);
-  // issue the loads of half h of chunk c (the wave's eight keys) into its staging:
-  // codes of key k at 16 CU k, its block scales at 1024 + 16 k; window bytes of key
-  // k at 16 WU k.  Padding slots read entry 0 / the first window token (masked).
-  auto stage = [&](int c, int h) {
+  // the loads of a whole chunk of selected entries (padding slots read entry 0,
+  // masked later)
+  auto stage_main = [&](int c) {
     const int ln = opaque(lane);
-    if (c < nm) {
-      if (ln < 8 * CU) {
-        const int e = max(s_ent[c * kKC + 8 * wave + ln / CU], 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_codes, (lds_ptr_t)my_stg, 16,
-                                                 e * (D / 2) + (D / 4) * h + 16 * (ln % CU), 0, 0, 0);
-      }
-      if (ln < 8) {
-        const int e = max(s_ent[c * kKC + 8 * wave + ln], 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_scales, (lds_ptr_t)(my_stg + 1024), 16,
-                                                 e * (D / 16) + (D / 32) * h, 0, 0, 0);
-      }
-    } else {
 #pragma unroll
-      for (int i = 0; i < NWI; ++i) {
-        const int u = 64 * i + ln, k = u / WU;
-        const int t = (c - nm) * kKC + 8 * wave + k;
-        const int slot = window_slot(win, t < n_swa ? t : 0, S);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_swa, (lds_ptr_t)(my_stg + 1024 * i), 16,
-                                                 slot * D + (D / 2) * h + 16 * (u % WU), 0, 0, 0);
-      }
+    for (int i = 0; i < NCI; ++i) {
+      const int u = 64 * i + ln;
+      const int e = max(s_ent[c * kKC + 8 * wave + u / CUK], 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_codes, (lds_ptr_t)(my_stg + 1024 * i), 16,
+                                               e * (D / 2) + 16 * (u % CUK), 0, 0, 0);
     }
+    if (ln < 8 * SUK) {
+      const int e = max(s_ent[c * kKC + 8 * wave + ln / SUK], 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_scales, (lds_ptr_t)(my_stg + SOFF), 16,
+                                               e * (D / 16) + 16 * (ln % SUK), 0, 0, 0);
+    }
+  };
+  // the loads of half h of a window chunk (padding slots read the first visible
+  // token, masked later)
+  auto stage_win = [&](int c, int h) {
+    const int ln = opaque(lane);
+#pragma unroll
+    for (int i = 0; i < NWI; ++i) {
+      const int u = 64 * i + ln, k = u / WU;
+      const int t = (c - nm) * kKC + 8 * wave + k;
+      const int slot = window_slot(win, t < n_swa ? t : 0, S);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_swa, (lds_ptr_t)(my_stg + 1024 * i), 16,
+                                               slot * D + (D / 2) * h + 16 * (u % WU), 0, 0, 0);
+    }
+  };
+  // what is staged a step ahead of its decode: a whole chunk of entries, or the
+  // first half of a window chunk
+  auto stage_first = [&](int c) {
+    if (c < nm) stage_main(c);
+    else stage_win(c, 0);
   };
   // the wave's staged loads have landed in LDS / its staging reads have returned
   auto wait_staged = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -179,14 +195,15 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
     uint8_t* rp = buf + r * KSTB + (r & 16) + (D / 2 * h + VPL * seg) * 2;
     if (main_chunk) {
       uint32_t cw[VPL / 8];  // 8 codes per word
+      const uint8_t* cp = my_stg + k * (D / 2) + (D / 4) * h + (VPL / 2) * seg;
       if constexpr (VPL == 32) {
-        const wu4_t v = *reinterpret_cast<const wu4_t*>(my_stg + 16 * CU * k + 16 * seg);
+        const wu4_t v = *reinterpret_cast<const wu4_t*>(cp);
         cw[0] = v[0]; cw[1] = v[1]; cw[2] = v[2]; cw[3] = v[3];
       } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(my_stg + 16 * CU * k + 8 * seg);
+        const uint2 v = *reinterpret_cast<const uint2*>(cp);
         cw[0] = v.x; cw[1] = v.y;
       }
-      const uint8_t* sp = my_stg + 1024 + 16 * k + (VPL / 16) * seg;
+      const uint8_t* sp = my_stg + SOFF + k * (D / 16) + (D / 32) * h + (VPL / 16) * seg;
       const uint32_t sw = VPL == 32 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : (uint32_t)*sp;
       const w2_t s01 = e4m3_pair<false>(sw);
       const w2_t mm[2] = {w2_t{s01[0], s01[0]}, w2_t{s01[1], s01[1]}};
@@ -255,18 +272,20 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
     }
   }
 
-  // ---- prologue: chunk 0 decoded, the first half of chunk 1 in flight
+  // ---- prologue: chunk 0 decoded, chunk 1 (or its first half) in flight
   if (n_chunks > 0) {
-    stage(0, 0);
+    stage_first(0);
     wait_staged();
     decode_half(buf_c, 0 < nm, 0);
-    wait_lds();
-    stage(0, 1);
-    wait_staged();
+    if (0 >= nm) {
+      wait_lds();
+      stage_win(0, 1);
+      wait_staged();
+    }
     decode_half(buf_c, 0 < nm, 1);
     if (1 < n_chunks) {
       wait_lds();
-      stage(1, 0);
+      stage_first(1);
     }
   }
   lds_barrier();
@@ -372,12 +391,12 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
     psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 4, 5), one2, psum, false);
     psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa, pa, 6, 7), one2, psum, false);
     l_run += main_chunk ? psum : psum * inv_swa;
-    // ---- first half of chunk c+1: decode what was staged, stage the second half
-    if (c + 1 < n_chunks) {
+    // ---- a window chunk c+1: decode its first half, stage the second
+    if (c + 1 < n_chunks && c + 1 >= nm) {
       wait_staged();
-      decode_half(buf_n, c + 1 < nm, 0);
+      decode_half(buf_n, false, 0);
       wait_lds();
-      stage(c + 1, 1);
+      stage_win(c + 1, 1);
     }
     // ---- O += P·V over the output tiles: one 16x16x32 MFMA per tile over both
     // key tiles (a 16x16x16 MFMA occupies the matrix unit as long as a 16x16x32
@@ -397,14 +416,16 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
         if (n + kPrefV < NO) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
-    // ---- second half of chunk c+1 (its buffer was last read in step c-1); the
-    // first half of chunk c+2 goes out
+    // ---- the rest of chunk c+1 (its buffer was last read in step c-1): both
+    // halves of a chunk of entries, the second half of a window chunk; then
+    // chunk c+2 (or its first half) goes out
     if (c + 1 < n_chunks) {
       wait_staged();
+      if (c + 1 < nm) decode_half(buf_n, true, 0);
       decode_half(buf_n, c + 1 < nm, 1);
       if (c + 2 < n_chunks) {
         wait_lds();
-        stage(c + 2, 0);
+        stage_first(c + 2);
       }
     }
     uint8_t* const t = buf_c;
@@ -442,8 +463,8 @@ __global__ __launch_bounds__(kWideThreads, 2) void sparse_attn_wide_kernel(
     float* __restrict__ out, float* __restrict__ lse) {
   // LDS: two chunk buffers (the chunk being attended, the next being decoded), the
   // waves' staging of raw chunk bytes, the row's selection
-  __shared__ __attribute__((aligned(16))) uint8_t kv[2 * (kKC * (2 * D + 32) + 16)];
-  __shared__ __attribute__((aligned(16))) uint8_t stg[kWideThreads / 64 * 2048];
+  __shared__ __attribute__((aligned(16))) uint8_t kv[2 * kKC * (2 * D + 32)];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[kWideThreads / 64 * kStageBytes];
   __shared__ int s_ent[kWideMaxSel];
   sparse_attn_wide_body<D>(kv, stg, s_ent, q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
                            q_pos, Tq, H_q, sm_log2, rows, head_groups, out, lse);
