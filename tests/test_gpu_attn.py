@@ -167,6 +167,7 @@ def test_few_rows_repeatable():
     (128, 256, 512, None, 128, 1.0, False),  # d = 256, two 64-head groups per row
     (64, 512, 512, None, 300, 0.37, True),   # window ring with positions, scaled window
     (64, 512, 64, 0, 128, 100.0, False),     # empty selection: window only
+    (64, 512, 512, 300, 0, 1.0, False),      # selection only: no window buffer
 ])
 def test_many_rows_wide_kernel(H, d, K, n_sel, S, swa_scale, prefill):
     """1,040 query rows (two sequences x 520 queries) take the many-rows kernel;
@@ -190,6 +191,27 @@ def test_many_rows_wide_kernel(H, d, K, n_sel, S, swa_scale, prefill):
         ref = sparse_attention(q[b, t], codes[b], scales[b], sel[b, t], swa[b], swa_scale, **pk)
         compare(out[b, t], ref)
         compare_lse(lse[b, t], q[b, t], codes[b], scales[b], sel[b, t], swa[b], swa_scale, **pk)
+
+
+def test_many_rows_nothing_visible():
+    """Many-rows launch where every other row sees no key at all (empty selection,
+    query position before the window's first token): those rows give a zero
+    output and lse = -inf, the rows beside them match the oracle."""
+    rng = np.random.default_rng(17)
+    B, Tq, H, d, N, K, S = 2, 520, 64, 512, 800, 64, 128
+    codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S, n_sel=0)
+    sel[:, 1::2, :40] = np.sort(rng.choice(N, 40, replace=False))
+    swa_pos0, n_win = 1000, 128
+    pos = np.where(np.arange(Tq) % 2 == 0, 900, 1000 + np.arange(Tq) % 128).astype(np.int32)[None].repeat(B, 0)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device="cuda")
+    out = bd().csa2_sparse_attn(dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa), q_pos=dev(pos),
+                                swa_pos0=swa_pos0, n_win=n_win, lse=lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(out[:, 0::2] == 0.0) and np.all(lse[:, 0::2] == -np.inf)
+    for b, t in [(0, 1), (1, 257), (1, 519)]:
+        pk = dict(q_pos=int(pos[b, t]), swa_pos0=swa_pos0, n_win=n_win)
+        compare(out[b, t], sparse_attention(q[b, t], codes[b], scales[b], sel[b, t], swa[b], **pk))
+        compare_lse(lse[b, t], q[b, t], codes[b], scales[b], sel[b, t], swa[b], **pk)
 
 
 def test_many_rows_wide_repeatable():
