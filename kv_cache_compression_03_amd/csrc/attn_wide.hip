@@ -110,14 +110,15 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
   const int hc = lane & 15, g = lane >> 4;  // MFMA row / column and lane group
   const int head0 = hgrp * kWideHeads + wave * 16;
 
-  // selection slots (ascending, -1 padded) rounded up to whole chunks; slots that
-  // are not a valid entry are masked
+  // selection slots (ascending, -1 padded) rounded up to whole chunks, held as the
+  // byte offset of the entry's codes (its scales sit at an eighth of it); slots
+  // that are not a valid entry are -1 and masked
   const int* srow = sel + (size_t)row * K;
   const int n_sel = N > 0 ? K : 0;
   const int nm = (n_sel + kKC - 1) / kKC;
   for (int i = tid; i < nm * kKC; i += kWideThreads) {
     const int v = i < n_sel ? srow[i] : -1;
-    s_ent[i] = (v >= 0 && v < N) ? v : -1;
+    s_ent[i] = (v >= 0 && v < N) ? v * (D / 2) : -1;
   }
   const WinRange win = window_of(q_pos, row, S, swa_pos0, n_win);
   const int n_swa = win.n;
@@ -155,14 +156,14 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
 #pragma unroll
     for (int i = 0; i < NCI; ++i) {
       const int u = 64 * i + ln;
-      const int e = max(s_ent[c * kKC + 8 * wave + u / CUK], 0);
+      const int eo = max(s_ent[c * kKC + 8 * wave + u / CUK], 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_codes, (lds_ptr_t)(my_stg + 1024 * i), 16,
-                                               e * (D / 2) + 16 * (u % CUK), 0, 0, 0);
+                                               eo + 16 * (u % CUK), 0, 0, 0);
     }
     if (ln < 8 * SUK) {
-      const int e = max(s_ent[c * kKC + 8 * wave + ln / SUK], 0);
+      const int eo = max(s_ent[c * kKC + 8 * wave + ln / SUK], 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_scales, (lds_ptr_t)(my_stg + SOFF), 16,
-                                               e * (D / 16) + 16 * (ln % SUK), 0, 0, 0);
+                                               (eo >> 3) + 16 * (ln % SUK), 0, 0, 0);
     }
   };
   // the loads of half h of a window chunk (padding slots read the first visible
@@ -331,19 +332,12 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
     const bool ok = main_chunk ? s_ent[c * kKC + kr] >= 0 : (c - nm) * kKC + kr < n_swa;
     const uint32_t vmask = (uint32_t)__ballot(ok);
     const float ks = main_chunk ? 1.0f : swa_scale;
-    const float fs = ks * sm_log2 * qs;
-    float lg[8];
+    const float fs = ks * sm_log2 * qs;  // > 0: base-2 logit = S^T * fs
+    float sv[8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = st[t][i] * fs;
-        // the logit is rounded on its own (as the reference maximum is), so the
-        // lazy bound below holds for the value exponentiated
-        asm("" : "+v"(x));
-        lg[4 * t + i] = x;
-      }
-    }
+      for (int i = 0; i < 4; ++i) sv[4 * t + i] = st[t][i];
     if (vmask != 0xFFFFFFFFu) {  // a chunk with masked keys (most have none)
       // lane-derived values are formed here, not kept in registers over the loop
       const uint32_t vm = vmask >> opaque(4 * g);
@@ -351,11 +345,14 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!((vm >> (16 * t + i)) & 1u)) lg[4 * t + i] = -INFINITY;
+          if (!((vm >> (16 * t + i)) & 1u)) sv[4 * t + i] = -INFINITY;
     }
-    float lmax = lg[0];
+    // the largest logit of the lane: the scale is positive, so it is the scaled
+    // largest S^T value
+    float smax = sv[0];
 #pragma unroll
-    for (int k = 1; k < 8; ++k) lmax = fmaxf(lmax, lg[k]);
+    for (int k = 1; k < 8; ++k) smax = fmaxf(smax, sv[k]);
+    const float lmax = smax * fs;
     // Lazy reference maximum: it moves only when a logit exceeds it by more than
     // 2^kLazy; the head's four lanes then agree on the new value.
     const bool up_lane = lmax > m_ref + kLazy || (m_ref == -INFINITY && lmax != -INFINITY);
@@ -379,10 +376,12 @@ __device__ __attribute__((always_inline)) void sparse_attn_wide_body(
     // P times the key scale, in fp16: p * ks = exp2(lg - (m_ref - log2 ks)); the row
     // sum gains the rounded values divided by ks.  While no key has been seen
     // (m_ref = -inf) every lg is -inf and p = 0.
+    // The exponent is formed in one rounding (S^T * fs - mp); it stays within a few
+    // units in the last place of the rounded logit minus mp, so p < 2^kLazy (1 + tiny).
     const float mp = m_ref == -INFINITY ? 0.0f : m_ref - (main_chunk ? 0.0f : log2_swa);
     w8_t pa;  // A operand of P·V: reduction slots 8g .. 8g+7 = keys 4g .. 4g+3 of each tile
 #pragma unroll
-    for (int k = 0; k < 8; ++k) pa[k] = (_Float16)__builtin_amdgcn_exp2f(lg[k] - mp);
+    for (int k = 0; k < 8; ++k) pa[k] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sv[k], fs, -mp));
     // the row sum adds the rounded probabilities (exact products in the dot)
     float psum = 0.0f;
     const w2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
