@@ -117,23 +117,6 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=5) -> float:
     return 2 * nbytes / t / 1e9
 
 
-def read_bandwidth(torch, nbytes=2 << 30, reps=5) -> float:
-    """Measured read-only rate (bytes read / s, GB/s) of a plain torch reduction over
-    `nbytes` of float32: a second reference beside the copy for read-bound kernels."""
-    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    torch.sum(x)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        torch.sum(x)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / reps
-    del x
-    return nbytes / t / 1e9
-
-
 def algorithmic_bytes(wl) -> dict:
     """Bytes a step must move at least: every Full layer streams the indexer keys
     of all entries; a Reindex layer gathers the keys of its pool; every layer reads
@@ -656,8 +639,6 @@ def main():
     traffic = traffic_record(f"traffic_index_scores_{wl.name}.txt", "index.hip", "common.h")
     copy_gbs = copy_bandwidth(torch)
     log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
-    read_gbs = read_bandwidth(torch)
-    log(f"device read (torch.sum over 2 GiB): {read_gbs:.0f} GB/s")
 
     out = {
         "metric": METRIC,
@@ -683,8 +664,7 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us": scan_s * 1e6, "algorithmic_bytes_per_launch": scan_bytes,
-                     "measured_copy_GB_s": copy_gbs, "frac_of_copy": achieved / copy_gbs,
-                     "measured_read_GB_s": read_gbs, "frac_of_read": achieved / read_gbs},
+                     "measured_copy_GB_s": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "step_hbm": {"algorithmic_bytes": ab["total"], "GB_s": ab["total"] / step_s / 1e9,
                      "frac": ab["total"] / step_s / 1e9 / HBM_PEAK_GBS, "breakdown": ab},
     }
