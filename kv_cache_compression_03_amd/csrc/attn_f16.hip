@@ -367,15 +367,24 @@ __global__ __launch_bounds__(HG2 * 256, 1) void sparse_attn_f16_kernel(
     l_run *= alpha;
     // P times the key scale, in fp16 (A operand of k-step t = elements 8t .. 8t+7):
     // p * ks = exp2(lg - (m_ref - log2 ks)), and the row sum gains sum(p * ks) / ks.
+    // The row sum adds the fp16-rounded values that P·V multiplies (exact products
+    // in the dot), so numerator and denominator carry the same probabilities and a
+    // key that takes all the weight is reproduced exactly.
     // While no key has been seen (m_ref = -inf) every lg is -inf and p = 0.
     const float mp = m_ref == -INFINITY ? 0.0f : m_ref - (main_chunk ? 0.0f : log2_swa);
-    float psum = 0.0f;
     f16x8_t pa[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pk = __builtin_amdgcn_exp2f(lg[i] - mp);
-      psum += pk;
-      pa[i / 8][i % 8] = (_Float16)pk;
+    for (int i = 0; i < 16; ++i) pa[i / 8][i % 8] = (_Float16)__builtin_amdgcn_exp2f(lg[i] - mp);
+    float psum = 0.0f;
+    {
+      const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa[t], pa[t], 0, 1), one2, psum, false);
+        psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa[t], pa[t], 2, 3), one2, psum, false);
+        psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa[t], pa[t], 4, 5), one2, psum, false);
+        psum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pa[t], pa[t], 6, 7), one2, psum, false);
+      }
     }
     l_run += main_chunk ? psum : psum * inv_swa;
     if (__ballot(up)) {
