@@ -6,9 +6,9 @@ Four kernels serve the call, and each is covered here:
 * up to 64 query rows with at most 512 selection slots, 128 visible window tokens,
   H_q a multiple of 16 and 0 < swa_scale <= 128: the few-rows kernel (a row's keys
   in one workgroup, no split partials);
-* at least 1024 (row, 64-head group) units, H_q a multiple of 64, at most 512
-  selection slots and 0 < swa_scale <= 128: the many-rows kernel (a workgroup per
-  row and 64 heads, no split partials);
+* otherwise at least 65 (row, 64-head group) units, H_q a multiple of 64, at most
+  512 selection slots and 0 < swa_scale <= 128: the many-rows kernel (a workgroup
+  per row and 64 heads, no split partials);
 * otherwise, H_q a multiple of 32 and 0 < swa_scale <= 128: the split-K fp16 kernel;
 * otherwise the split-K bf16 kernel."""
 import numpy as np
@@ -128,13 +128,15 @@ def test_swa_scale_and_prefill_positions(swa_scale):
 
 
 @pytest.mark.parametrize("H,K,n_sel,S", [
-    (64, 512, None, 128),    # split-K fp16 kernel (more than 128 rows)
+    (96, 512, None, 128),    # split-K fp16 kernel (H_q a multiple of 32, not of 64)
     (48, 512, None, 128),    # split-K bf16 kernel (H_q not a multiple of 32)
-    (64, 300, 77, 77),       # split-K fp16 kernel, ragged selection and window
+    (96, 300, 77, 77),       # split-K fp16 kernel, ragged selection and window
+    (64, 300, 77, 77),       # the same rows at 64 heads: the many-rows kernel
 ])
 def test_many_rows_split_kernels(H, K, n_sel, S):
     """136 query rows (two sequences x 68 queries, more than the few-rows kernel
-    takes) run the split-K kernels; sampled rows against the oracle."""
+    takes) run the split-K kernels, or the many-rows kernel at 64 heads; sampled
+    rows against the oracle."""
     rng = np.random.default_rng(H + K + S)
     B, Tq, d, N = 2, 68, 512, 2000
     codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S, n_sel)
