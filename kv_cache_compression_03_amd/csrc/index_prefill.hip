@@ -23,6 +23,9 @@
 
 namespace csa2 {
 
+// cache-policy operand of a buffer store on gfx950: non-temporal (streaming)
+constexpr int kStoreNonTemporal = 2;
+
 constexpr int kPfWaves = 4;
 constexpr int kPfRows = 256;  // (query, head) rows per workgroup, 64 per wave
 constexpr int kPfKeys = 64;   // keys per staged tile
@@ -241,11 +244,14 @@ __global__ __launch_bounds__(kPfWaves * 64, 2) void index_prefill_kernel(
           if (j >= nv[n]) pv[n][ct] = -INFINITY;
         }
     }
+    // streaming stores (non-temporal): the scores of a chunk are far larger than
+    // the caches, and keeping them out leaves L2 to the keys every query block
+    // re-reads (-2.5 % per launch measured)
 #pragma unroll
     for (int n = 0; n < NG; ++n)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pv[n][ct]), srsc, of[n][ct], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pv[n][ct]), srsc, of[n][ct], 0, kStoreNonTemporal);
     __builtin_amdgcn_sched_barrier(0);  // stash after the stores
     // buffer buf^1 was last read in pass tile-1, before that pass's barrier
     CSA2_PF_STASH(buf ^ 1)

@@ -42,6 +42,7 @@ def test_scores_and_topk(B, N, h_i, d_i):
     (3, 16, 64),    # one query per tile
     (9, 4, 128),    # four queries per tile, the last tile partial
     (2, 8, 64),     # one tile
+    (3, 8, 128),    # two query tiles, the second partial
 ])
 def test_scores_with_positions(Tq, h_i, d_i):
     """Several queries per sequence (drafted positions, prefill rows below the
@@ -191,6 +192,7 @@ def test_reindex():
     (2, 1, 5000, 512, True, "gauss"),      # short rows: selected whole
     (2, 1, 300000, 512, True, "ties"),     # integer scores: candidates overflow, exact fallback
     (2, 3, 50000, 512, False, "gauss"),    # three queries per sequence at their own positions
+    (1, 8, 30000, 512, False, "gauss"),    # eight queries: four query tiles per wave, span maxima per tile
     (1, 1, 128 * 2048 + 77, 512, True, "gauss"),  # just over PB blocks, ragged last block
 ])
 def test_full_layer_select(B, Tq, N, K, pool, kind):
