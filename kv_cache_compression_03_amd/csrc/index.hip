@@ -14,6 +14,14 @@
 // products are unchanged.  The ReLU / head-weight / head-sum epilogue runs on the MFMA
 // output: a lane holds 4 heads of one query for one entry, and one or two
 // cross-lane adds finish the head sum.
+//
+// Scores leave through non-temporal stores.  They are few beside the keys (4 B
+// per query against 256 B per entry) but cost far more than their share: the
+// writes, spread thinly through a saturated read stream, made the 8 x 1M scan
+// about 12 % slower than the same kernel with its stores removed, and whether a
+// wave writes one or two lines per batch made no difference.  The non-temporal
+// hint takes 1 % of that back at one query per sequence and 2.5-3 % at three to
+// six queries.
 #include "common.h"
 #include "internal.h"
 
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(kScanWaves * 64, QG == 1 ? 7 : 1) void index_scores
         if (HI >= 8) v += __shfl_xor(v, 16);
         if (HI >= 16) v += __shfl_xor(v, 32);
         const float sv = (ent_ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
-        if (writer[qg] && e < L) srow[qg][e] = sv;
+        if (writer[qg] && e < L) __builtin_nontemporal_store(sv, &srow[qg][e]);
         if constexpr (TM) bm[qg] = fmaxf(bm[qg], e < L ? sv : -INFINITY);
       }
     }
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void i
         if (HI >= 8) v += __shfl_xor(v, 16);
         if (HI >= 16) v += __shfl_xor(v, 32);
         const float sv = (ent_ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
-        if (writer[qg] && e < L) srow0[(size_t)qg * QPT * L + e] = sv;
+        if (writer[qg] && e < L) __builtin_nontemporal_store(sv, &srow0[(size_t)qg * QPT * L + e]);
         if constexpr (TM) bm = fmaxf(bm, e < L ? sv : -INFINITY);
       }
       if constexpr (TM) {
