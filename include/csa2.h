@@ -252,16 +252,23 @@ CSA2_API int csa2_index_reindex(const void* q_idx, const float* w, const void* k
  *          every one of the S slots is visible.
  *   out    [B, Tq, H_q, d] f32;  lse [B, Tq, H_q] f32 natural-log sum-exp or NULL
  *   sm_scale <= 0 selects 1/sqrt(d).
- *   ws     >= csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) bytes (0 when a row is
- *          not split over its keys)
+ *   ws     >= csa2_sparse_attn_workspace(B, Tq, H_q, d, K, S) bytes, device memory
+ *          owned by the caller (NULL when that is 0); its contents need no set-up
  * Limits: d in {256, 512}, H_q % 16 == 0, K <= 2048.
- * Kernels: up to 64 query rows (decode steps) with at most 512 selection slots,
- * 128 visible window tokens, 0 < swa_scale <= 128 and 16-byte aligned q, out and
- * caches, all keys of a row are handled inside one workgroup per (row, 16 heads,
- * part of the dims), with no split partials and no merge launch (fp16 products,
- * probabilities with 11 significant bits, queries scaled into fp16 by a power of
- * two per head); the workspace is then unused.  Otherwise a split-K kernel and a
- * merge launch.
+ * Kernels, for 16-byte aligned q, out and caches, at most 512 selection slots
+ * and 0 < swa_scale <= 128 (fp16 products, probabilities with 11 significant
+ * bits, queries scaled into fp16 by a power of two per head):
+ *   - up to 8 query rows at H_q = 64 and d = 512 with at most 128 visible window
+ *     tokens: two launches; a workgroup per (row, 32-key chunk) scores the chunk
+ *     once for all heads and leaves fp16 probabilities, the chunk's (max, sum)
+ *     per head and its decoded values in ws, then a workgroup per (row, 16
+ *     heads, 64 dims) merges the chunks and forms the output;
+ *   - otherwise up to 64 query rows with at most 128 visible window tokens: all
+ *     keys of a row inside one workgroup per (row, 16 heads, part of the dims),
+ *     no partials, ws unused;
+ *   - otherwise, with H_q % 64 == 0 and at least 65 (row, 64 heads) units: a
+ *     workgroup per (row, 64 heads), no partials, ws unused.
+ * Otherwise a split-K kernel and a merge launch, the partials in ws.
  * Precision: products are exact (entries, window values and probabilities are
  * carried in fp16 or bf16, both exact for the decoded values) and accumulate in
  * fp32.  When H_q % 32 == 0, 0 < swa_scale <= 128 and codes, scales and swa are

@@ -17,7 +17,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
 
 SOURCES = ["api.cpp", "quant.hip", "compress.hip", "index.hip", "index_prefill.hip", "topk.hip",
-           "attn.hip", "attn_f16.hip", "attn_rows.hip", "attn_wide.hip"]
+           "attn.hip", "attn_f16.hip", "attn_rows.hip", "attn_split.hip",
+           "attn_wide.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -41,6 +41,9 @@ namespace csa2 {
 #ifndef CSA2_ROWS_MAX
 #define CSA2_ROWS_MAX 64  // query rows up to which the few-rows kernel runs (measured: faster up to 64)
 #endif
+#ifndef CSA2_SPLIT_ROWS_MAX
+#define CSA2_SPLIT_ROWS_MAX 8  // query rows up to which the two-launch few-rows path runs (measured: faster up to 8)
+#endif
 #ifndef CSA2_ROWS_DP4_MAX
 #define CSA2_ROWS_DP4_MAX 16  // rows up to which it splits the output dims in four (d = 512)
 #endif
@@ -79,6 +82,7 @@ AttnPlan attn_plan(int B, int Tq, int H_q, int K, int L_max) {
   long long want = (CSA2_ATTN_TARGET_WGS + base - 1) / base;
   int ns = (int)(want < 1 ? 1 : (want > max_chunks ? max_chunks : want));
   if (ns > kMaxSplits) ns = kMaxSplits;
+  if (ns < 1) ns = 1;  // a row with no keys at all (no selection slots, no window)
   p.chunks_per_split = (max_chunks + ns - 1) / ns;
   if (p.chunks_per_split < 1) p.chunks_per_split = 1;
   p.n_splits = (max_chunks + p.chunks_per_split - 1) / p.chunks_per_split;
@@ -87,10 +91,17 @@ AttnPlan attn_plan(int B, int Tq, int H_q, int K, int L_max) {
 
 size_t attn_ws_bytes(int B, int Tq, int H_q, int d, int K, int L_max) {
   AttnPlan p = attn_plan(B, Tq, H_q, K, L_max);
-  if (p.n_splits <= 1) return 0;
   const size_t rows = (size_t)B * Tq;
-  return align256(rows * p.n_splits * H_q * d * sizeof(float)) +
-         align256(rows * p.n_splits * H_q * 2 * sizeof(float));
+  size_t need = 0;
+  if (p.n_splits > 1)
+    need = align256(rows * p.n_splits * H_q * d * sizeof(float)) +
+           align256(rows * p.n_splits * H_q * 2 * sizeof(float));
+  // the two-launch few-rows path (its window bound is checked at launch)
+  if (rows <= CSA2_SPLIT_ROWS_MAX && attn_split_supported(H_q, d, K, 0, 0, false, 1.0f)) {
+    const size_t s = attn_split_ws_bytes((int)rows, K, L_max - K);
+    need = s > need ? s : need;
+  }
+  return need;
 }
 
 template <int D, int HG>
@@ -455,6 +466,14 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* codes, const uin
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(scales) |
                            reinterpret_cast<uintptr_t>(swa) | reinterpret_cast<uintptr_t>(q) |
                            reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+  // Few rows at 64 heads and 512 dims: each key decoded and scored once per row,
+  // then P·V over (row, 16 heads, 64 dims) workgroups.
+  // (a call with no keys at all needs no workspace: only the second launch runs)
+  if (aligned16 && rows <= CSA2_SPLIT_ROWS_MAX &&
+      attn_split_supported(H_q, d, K, S, n_win, q_pos != nullptr, swa_scale) &&
+      (ws != nullptr || attn_split_ws_bytes(rows, K, S) == 0))
+    return launch_sparse_attn_split(q, codes, scales, N, sel, K, swa, swa_scale, S, swa_pos0, n_win,
+                                    q_pos, Tq, sm_log2_rows, rows, ws, out, lse, st);
   // Few rows (decode steps): every key of a row inside one workgroup per (row, 16
   // heads, output-dim part), no split partials and no combine launch.
   if (aligned16 && rows <= CSA2_ROWS_MAX &&

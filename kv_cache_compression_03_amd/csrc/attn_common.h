@@ -1,5 +1,5 @@
 // Pieces shared by the sparse-attention kernels (attn.hip, attn_f16.hip, attn_rows.hip,
-// attn_wide.hip).
+// attn_split.hip, attn_wide.hip).
 #pragma once
 
 #include "common.h"
@@ -83,6 +83,19 @@ hipError_t launch_sparse_attn_rows(const uint16_t* q, const uint8_t* codes, cons
                                    int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,
                                    int H_q, int d, float sm_log2, int rows, int dp, float* out,
                                    float* lse, hipStream_t st);
+
+// few-rows path in two launches (attn_split.hip): a workgroup per (row, 32-key
+// chunk) scores the chunk for all 64 heads, then a workgroup per (row, 16 heads,
+// 64 dims) forms P·V.  Usable when H_q is 64, d is 512, at most 512 selection
+// slots and 128 visible window tokens, and 0 < swa_scale <= 128; needs
+// attn_split_ws_bytes(rows, K, S) bytes of workspace.
+bool attn_split_supported(int H_q, int d, int K, int S, int n_win, bool with_pos, float swa_scale);
+size_t attn_split_ws_bytes(int rows, int K, int S);
+hipError_t launch_sparse_attn_split(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                    int N, const int* sel, int K, const uint8_t* swa, float swa_scale,
+                                    int S, long long swa_pos0, int n_win, const int* q_pos, int Tq,
+                                    float sm_log2, int rows, void* ws, float* out, float* lse,
+                                    hipStream_t st);
 
 // many-rows kernel (attn_wide.hip): a workgroup per (row, 64 heads), each wave 16
 // heads over all dims, no split partials.  Usable when H_q is a multiple of 64, d

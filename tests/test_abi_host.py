@@ -39,6 +39,13 @@ def test_workspace_queries_are_host_only():
     assert bd.csa2_index_full_workspace(1, 8192, 16384, 8, 128, 0, 0, 8, 512) < 1 << 20
     assert bd.csa2_sparse_attn_workspace(8192, 1, 64, 512, 512, 8319) == 0   # one split
     assert bd.csa2_sparse_attn_workspace(8, 1, 64, 512, 512, 128) > 0
+    # few rows at 64 heads x 512 dims: the two-launch path keeps, per (row, 32-key
+    # chunk), 4 KB of probabilities, 512 B of (max, sum) and 32 KB of values
+    assert bd.csa2_sparse_attn_workspace(1, 4, 64, 512, 40, 100) >= 4 * 6 * (4096 + 512 + 32768)
+    # no keys at all (no selection slots, no window): no split and no workspace,
+    # and no division by the zero chunk count
+    assert bd.csa2_sparse_attn_workspace(1, 4, 64, 512, 0, 0) == 0
+    assert bd.csa2_sparse_attn_workspace(2, 1, 32, 256, 0, 0) == 0
 
 
 def test_status_strings():

@@ -2,10 +2,13 @@
 Bar: max |gpu - oracle| <= 2e-3 x RMS(oracle output) (fp32 accumulation); the
 log-sum-exp within 2e-4 x (1 + |oracle|).
 
-Four kernels serve the call, and each is covered here:
-* up to 64 query rows with at most 512 selection slots, 128 visible window tokens,
-  H_q a multiple of 16 and 0 < swa_scale <= 128: the few-rows kernel (a row's keys
-  in one workgroup, no split partials);
+Five kernel paths serve the call, and each is covered here:
+* up to 8 query rows at 64 heads and d = 512 with at most 512 selection slots,
+  128 visible window tokens and 0 < swa_scale <= 128: the two-launch few-rows path
+  (each key scored once per row, then P·V over (row, 16 heads, 64 dims));
+* otherwise up to 64 query rows with at most 512 selection slots, 128 visible
+  window tokens, H_q a multiple of 16 and 0 < swa_scale <= 128: the few-rows
+  kernel (a row's keys in one workgroup, no split partials);
 * otherwise at least 65 (row, 64-head group) units, H_q a multiple of 64, at most
   512 selection slots and 0 < swa_scale <= 128: the many-rows kernel (a workgroup
   per row and 64 heads, no split partials);
@@ -66,6 +69,9 @@ def compare_lse(lse, q, codes, scales, sel, swa, swa_scale=1.0, q_pos=None, swa_
     (1, 64, 512, 300, 512, 128, None),      # K >= N: every entry selected
     (2, 64, 512, 1000, 100, 0, None),       # no window
     (2, 32, 512, 1000, 512, 128, 0),        # empty selection: window only
+    (2, 64, 512, 1000, 512, 128, 0),        # the same at 64 heads (every slot masked)
+    (3, 64, 512, 1000, 0, 128, None),       # no selection slots at all (K = 0)
+    (1, 64, 512, 3000, 40, 100, None),      # one short chunk of entries, ragged window
     (2, 64, 512, 4000, 512, 128, 77),       # ragged selection
     (9, 64, 512, 3000, 512, 128, None),     # more rows (different split plan)
     (2, 64, 256, 2048, 512, 128, None),     # d = 256, two 32-head groups per workgroup
@@ -107,10 +113,11 @@ def test_query_magnitudes(q_exp):
         compare_lse(lse[b, 0], q[b, 0], codes[b], scales[b], sel[b, 0], swa[b])
 
 
+@pytest.mark.parametrize("H", [32, 64])
 @pytest.mark.parametrize("swa_scale", [0.37, 100.0, 200.0, -0.5])   # 200, -0.5: bf16 kernel
-def test_swa_scale_and_prefill_positions(swa_scale):
-    rng = np.random.default_rng(11)
-    B, Tq, H, d, N, K, S, n_win = 1, 7, 32, 512, 4000, 64, 300, 128
+def test_swa_scale_and_prefill_positions(swa_scale, H):
+    rng = np.random.default_rng(11 + H)
+    B, Tq, d, N, K, S, n_win = 1, 7, 512, 4000, 64, 300, 128
     codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S)
     swa_pos0 = 1000
     lse = torch.empty(B, Tq, H, dtype=torch.float32, device="cuda")
@@ -148,6 +155,28 @@ def test_many_rows_split_kernels(H, K, n_sel, S):
         ref = sparse_attention(q[b, t], codes[b], scales[b], sel[b, t], swa[b])
         compare(out[b, t], ref)
         compare_lse(lse[b, t], q[b, t], codes[b], scales[b], sel[b, t], swa[b])
+
+
+@pytest.mark.parametrize("S", [128, 0])
+def test_few_rows_nothing_visible(S):
+    """Few rows at 64 heads where some rows see no key at all (no selection slots;
+    a query position before the window's first token, or no window buffer): those
+    rows give a zero output and lse = -inf, the others match the oracle."""
+    rng = np.random.default_rng(23 + S)
+    B, Tq, H, d, N, K = 1, 4, 64, 512, 800, 0
+    codes, scales, q, sel, swa = make_case(rng, B, Tq, H, d, N, K, S)
+    swa_pos0, n_win = 1000, 128
+    pos = np.array([[500, 1000, 1063, 999]], np.int32)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device="cuda")
+    out = bd().csa2_sparse_attn(dev_bf16(q), dev(codes), dev(scales), dev(sel), dev(swa), q_pos=dev(pos),
+                                swa_pos0=swa_pos0, n_win=n_win, lse=lse)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    blind = [0, 3] if S > 0 else [0, 1, 2, 3]
+    assert np.all(out[0, blind] == 0.0) and np.all(lse[0, blind] == -np.inf)
+    for t in sorted(set(range(Tq)) - set(blind)):
+        pk = dict(q_pos=int(pos[0, t]), swa_pos0=swa_pos0, n_win=n_win)
+        compare(out[0, t], sparse_attention(q[0, t], codes[0], scales[0], sel[0, t], swa[0], **pk))
+        compare_lse(lse[0, t], q[0, t], codes[0], scales[0], sel[0, t], swa[0], **pk)
 
 
 def test_few_rows_repeatable():

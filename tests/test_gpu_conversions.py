@@ -12,9 +12,10 @@ that key as the kernel decoded it.  These tests make every decoded value visible
   swa_scale, exactly at swa_scale 1; at 0.37 the scale enters through the
   probability (a power of two split off in fp16 / a bf16 pair), so the bound is
   2^-10 relative, far below the 1/16 step between neighbouring E4M3 values;
-* every kernel: up to 64 query rows the few-rows kernel (32 and 48 heads); with
-  136 rows (each query cycling over the entries / window tokens) the split-K
-  kernels, 32 heads (fp16) and 48 heads (bf16).
+* every kernel: few rows take the one-launch few-rows kernel (32 and 48 heads)
+  or the two-launch few-rows path (64 heads); with 136 rows (each query cycling
+  over the entries / window tokens) the split-K kernels, 32 heads (fp16) and 48
+  heads (bf16), or the many-rows kernel (64 heads).
 """
 import numpy as np
 import pytest
@@ -52,7 +53,7 @@ def all_code_entries():
 
 
 @pytest.mark.parametrize("rows", [8, 136])
-@pytest.mark.parametrize("H_q", [32, 48])
+@pytest.mark.parametrize("H_q", [32, 48, 64])
 def test_every_fp4_code_under_every_scale(H_q, rows):
     codes, scales = all_code_entries()
     n = codes.shape[0]
@@ -73,7 +74,7 @@ def test_every_fp4_code_under_every_scale(H_q, rows):
 
 
 @pytest.mark.parametrize("Tq", [4, 136])
-@pytest.mark.parametrize("H_q", [32, 48])
+@pytest.mark.parametrize("H_q", [32, 48, 64])
 @pytest.mark.parametrize("swa_scale", [1.0, 0.37])
 def test_every_fp8_window_code(H_q, swa_scale, Tq):
     tok = np.stack([FINITE_E4M3[(np.arange(D) + 37 * t) % FINITE_E4M3.shape[0]] for t in range(Tq)])
