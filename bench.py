@@ -659,8 +659,7 @@ def main():
                    "full_top_k": "inside the pool" if args.full_in_pool else "global",
                    "graph": not args.no_graph, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
-                     "kernel": ("index_scores_mq_kernel" if (wl.Tq * wl.h_i + 15) // 16 >= 2 else "index_scores_kernel")
-                               + " (Full-layer indexer scan)",
+                     "kernel": scan_kernel_name(wl) + " (Full-layer indexer scan)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "launch_us": scan_s * 1e6, "algorithmic_bytes_per_launch": scan_bytes,
@@ -675,6 +674,18 @@ def main():
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def scan_kernel_name(wl) -> str:
+    """The kernel csa2_index_full launches for the workload's scan: several query
+    tiles per sequence take the multi-query kernel; one query over rows of at least
+    2^19 entries (a multiple of 32, at least one 32-entry batch per CU) the scan
+    that holds its scores in LDS; otherwise the one-shot scan."""
+    if (wl.Tq * wl.h_i + 15) // 16 >= 2:
+        return "index_scores_mq_kernel"
+    if wl.Tq == 1 and wl.N >= 1 << 19 and wl.N % 32 == 0 and 256 <= wl.B * wl.N // 32 <= 256 * 1152:
+        return "index_scores_persist_kernel"
+    return "index_scores_kernel"
 
 
 if __name__ == "__main__":

@@ -344,6 +344,142 @@ __global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void i
   }
 }
 
+
+// One query per sequence over long rows (at least kPersMinL entries): one
+// workgroup per CU holds the scores it computes in LDS while its keys stream in
+// and writes them in one burst at the end.  Score writes spread thinly through
+// the key stream cost far more than their bytes (about 12 % of the 8 x 1M scan);
+// written at the end they cost about their bytes, and the scores the selection
+// kernels read next are still in the memory-side cache.  The 32-entry batches are
+// dealt round robin over the whole grid (batch F to workgroup F mod G), so all
+// CUs move through the keys together, as the one-shot waves of the other scan do
+// (a contiguous share per workgroup, 256 streams at once, was 7 % slower).  Each
+// wave prefetches its next batch while it scores the current one; its batches
+// change sequence only every L/32/G of them, and the query is reloaded then.
+// Measured against index_scores_kernel: 8 x 1M 346 vs 350-385 us, equal at 512K
+// and 256K per row, 4 % slower at 128K and below (the query reloads), hence
+// kPersMinL.
+constexpr int kPersThreads = 1024;
+constexpr int kPersWaves = kPersThreads / 64;
+constexpr int kPersMaxBatches = 1152;   // 32-entry batches a workgroup holds (144 KB of LDS)
+constexpr int kPersMinL = 1 << 19;
+
+template <int HI, int DI, bool TM>
+__global__ __launch_bounds__(kPersThreads, 1) void index_scores_persist_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, const int* __restrict__ q_pos, int m, int N, int L,
+    int nbat, float* __restrict__ scores, float* __restrict__ tmax) {
+  static_assert(kScanBatch == 2 && kTmaxSpan == 32, "32-entry batches of two 16-key tiles");
+  constexpr int KS = DI / 32;
+  __shared__ __attribute__((aligned(16))) float s_sc[kPersMaxBatches * 32];
+  __shared__ float s_tm[kPersMaxBatches];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int bpr = L / 32;                       // batches per sequence
+  const int nloc = (nbat - wg + G - 1) / G;     // local slots: batch wg + G t, t < nloc
+  // lane group 0 holds query 0's score of each key after the head sum
+  const bool writer = g == 0;
+
+  // the query of the current sequence: A row col = head col (rows past h_i zero)
+  int bq = -1, nvis = L;
+  bf16x8_t qa[KS];
+  float wq[4];
+  auto set_seq = [&](int b) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(q_idx + ((size_t)b * HI + (col < HI ? col : 0)) * DI);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 v = qrow[s * 4 + g];
+      qa[s] = as_bf16x8(col < HI ? v : make_uint4(0, 0, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      const float x = w[(size_t)b * HI + (r < HI ? r : 0)];
+      wq[i] = r < HI ? x : 0.0f;
+    }
+    nvis = L;
+    if (q_pos != nullptr) {
+      const long long p = q_pos[b];
+      const long long nv = (p + 1) / m;
+      nvis = (int)(nv < 0 ? 0 : (nv > L ? L : nv));
+    }
+    bq = b;
+  };
+  struct Batch {
+    uint4 kv[kScanBatch][KS];
+  };
+  // keys of local slot t (past the last slot: the last one again, masked later)
+  auto load = [&](int t, Batch& bt) {
+    const int F = wg + G * min(t, nloc - 1);
+    const int b = F / bpr, e = (F - b * bpr) * 32;
+    const uint16_t* kb = k_idx + (size_t)b * N * DI;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const uint4* kr = reinterpret_cast<const uint4*>(kb + (size_t)(e + 16 * u + col) * DI);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) bt.kv[u][s] = kr[s * 4 + g];
+    }
+  };
+  auto score = [&](int t, const Batch& bt) {
+    const bool live = t < nloc;
+    const int F = wg + G * min(t, nloc - 1);
+    const int b = F / bpr, e = (F - b * bpr) * 32;
+    if (b != bq) set_seq(b);  // uniform
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma16x16x32(qa[s], as_bf16x8(bt.kv[u][s]), acc);
+      float v = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(wq[i], fmaxf(acc[i], 0.0f), v);
+      if (HI >= 8) v += __shfl_xor(v, 16);
+      if (HI >= 16) v += __shfl_xor(v, 32);
+      const float sv = (e + 16 * u + col < nvis) ? v : -INFINITY;
+      if (writer && live) s_sc[32 * t + 16 * u + col] = sv;
+      if constexpr (TM) bm = fmaxf(bm, sv);
+    }
+    if constexpr (TM) {
+      const float tv = row16_max(bm);  // query 0's maximum sits in lane 0
+      if (lane == 0 && live) s_tm[t] = tv;
+    }
+  };
+
+  Batch b0, b1;
+  load(wave, b0);
+  for (int t = wave; t < nloc; t += 2 * kPersWaves) {
+    load(t + kPersWaves, b1);
+    score(t, b0);
+    load(t + 2 * kPersWaves, b0);
+    score(t + kPersWaves, b1);
+  }
+  __syncthreads();
+  // slot t holds batch F = wg + G t, whose 32 scores sit at F * 32 (Tq = 1)
+  for (int i = threadIdx.x; i < nloc * 8; i += kPersThreads) {
+    const int t = i >> 3, k = (i & 7) * 4;
+    const size_t F = (size_t)wg + (size_t)G * t;
+    *reinterpret_cast<float4*>(scores + F * 32 + k) = *reinterpret_cast<const float4*>(s_sc + 32 * t + k);
+  }
+  if constexpr (TM) {
+    for (int t = threadIdx.x; t < nloc; t += kPersThreads) tmax[(size_t)wg + (size_t)G * t] = s_tm[t];
+  }
+}
+
+// compute units of the current device (looked up once per device)
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                                const int* gather, const int* gather_len, const int* q_pos, int m,
                                int B, int Tq, int N, int L, int h_i, int d_i, float* scores,
@@ -351,6 +487,30 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   if (B == 0 || Tq == 0 || L == 0) return hipSuccess;
   if (tmax == nullptr && L == N && index_prefill_supported(Tq, N, h_i, d_i, gather))
     return launch_index_prefill(q_idx, w, k_idx, q_pos, m, B, Tq, N, h_i, d_i, scores, st);
+  // one query per sequence over long rows: the LDS-held scan
+  const int cus = device_cus();
+  const long long nbat = (long long)B * (L / 32);
+  if (Tq == 1 && gather == nullptr && L == N && L % 32 == 0 && L >= kPersMinL && cus > 0 &&
+      nbat >= cus && nbat <= (long long)cus * kPersMaxBatches &&
+      (reinterpret_cast<uintptr_t>(scores) & 15) == 0) {
+#define CSA2_PERS(HI_, DI_)                                                                        \
+  do {                                                                                             \
+    if (tmax)                                                                                      \
+      hipLaunchKernelGGL((index_scores_persist_kernel<HI_, DI_, true>), dim3(cus), dim3(kPersThreads), \
+                         0, st, q_idx, w, k_idx, q_pos, m, N, L, (int)nbat, scores, tmax);          \
+    else                                                                                           \
+      hipLaunchKernelGGL((index_scores_persist_kernel<HI_, DI_, false>), dim3(cus), dim3(kPersThreads), \
+                         0, st, q_idx, w, k_idx, q_pos, m, N, L, (int)nbat, scores, tmax);          \
+  } while (0)
+    if (h_i == 8 && d_i == 128) CSA2_PERS(8, 128);
+    else if (h_i == 8 && d_i == 64) CSA2_PERS(8, 64);
+    else if (h_i == 4 && d_i == 128) CSA2_PERS(4, 128);
+    else if (h_i == 4 && d_i == 64) CSA2_PERS(4, 64);
+    else if (h_i == 16 && d_i == 128) CSA2_PERS(16, 128);
+    else CSA2_PERS(16, 64);
+#undef CSA2_PERS
+    return hipGetLastError();
+  }
   const int qpt = 16 / h_i;
   const int qtiles = (Tq + qpt - 1) / qpt;
   // query tiles per wave: every key tile is read once for up to four of them

@@ -69,6 +69,29 @@ def test_scores_with_positions(Tq, h_i, d_i):
             check_topk(sel[b, t], ref, 512, n_vis=n)
 
 
+@pytest.mark.parametrize("N,h_i,d_i", [(1 << 19, 8, 128), (1 << 19, 4, 64), ((1 << 19) + 32, 16, 128),
+                                       ((1 << 19) + 1, 8, 128)])
+def test_long_row_scan(N, h_i, d_i):
+    """One query per sequence over rows of half a million entries and more (the
+    scan that holds each workgroup's scores in LDS and writes them at the end;
+    a row length that is not a multiple of 32 takes the other scan): every score,
+    with a visible prefix on the second sequence."""
+    B, m = 2, 2
+    rng = np.random.default_rng(N + h_i + d_i)
+    q = rand_bf16(rng, (B, 1, h_i, d_i))
+    w = rng.random((B, 1, h_i)).astype(np.float32)
+    k = rand_bf16(rng, (B, N, d_i))
+    pos = np.array([[2 * N + 5], [600001]], np.int32)   # all visible; the first 300,001
+    sc = bd().csa2_index_full(dev_bf16(q), dev(w), dev_bf16(k), q_pos=dev(pos), m=m)
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy()
+    for b in range(B):
+        n = visible_count(int(pos[b, 0]), N, m)
+        ref = index_scores(q[b, 0], w[b, 0], k[b])
+        assert np.all(np.isneginf(sc[b, 0, n:]))
+        assert np.all(np.abs(sc[b, 0, :n] - ref[:n]) <= score_tol(q[b, 0], w[b, 0], k[b])[:n])
+
+
 @pytest.mark.parametrize("B,Tq,N,h_i,d_i,m,pos", [
     (1, 100, 5000, 8, 128, 2, "rand"), (2, 140, 4100, 4, 64, 1, "rand"),
     (1, 40, 9000, 16, 128, 2, "causal"), (1, 64, 300, 8, 64, 1, "none"),
@@ -194,6 +217,7 @@ def test_reindex():
     (2, 3, 50000, 512, False, "gauss"),    # three queries per sequence at their own positions
     (1, 8, 30000, 512, False, "gauss"),    # eight queries: four query tiles per wave, span maxima per tile
     (1, 1, 128 * 2048 + 77, 512, True, "gauss"),  # just over PB blocks, ragged last block
+    (2, 1, 1 << 19, 512, True, "ties"),    # long rows (scores held in LDS until the end), ties
 ])
 def test_full_layer_select(B, Tq, N, K, pool, kind):
     """csa2_index_full with the pool and the layer's Top-K: both are functions of the
