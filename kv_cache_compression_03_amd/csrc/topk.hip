@@ -374,8 +374,8 @@ CSA2_DEV int block_scan_sel(int v, int* wsum, int* total) {
 
 // ---------------------------------------------------------------- histogram select
 //
-// Exact choice of the k best of a workgroup's values (each thread holds M, with
-// their indices; key order = value desc, index asc) in few barriers:
+// Exact choice of the k best of a row's values (thread t holds the M values
+// t + kSelThreads * u; key order = value desc, index asc) in few barriers:
 //   1. min and max of the values;
 //   2. a histogram of kHistBuckets buckets of [min, max] under a monotone map
 //      (value_bucket: equal values share a bucket, a larger value never falls in
@@ -386,8 +386,9 @@ CSA2_DEV int block_scan_sel(int v, int* wsum, int* total) {
 //      when they are few, else by the radix select on unique 64-bit keys, else
 //      (more than kTopkCap in one bucket: a row of equal or tightly packed
 //      values) by the exact whole-row select.
-// Writes the k chosen indices (unordered) to chosen[0 .. k).  LDS: keys holds
-// kTopkCap keys (its first 8 KB also serve as the histogram).
+// Marks the k chosen indices in the bitmap (bit i & 31 of word i >> 5; all words
+// are written).  LDS: keys holds kTopkCap keys (its first 8 KB also serve as the
+// histogram).
 constexpr int kHistBuckets = 2 * kSelThreads;
 constexpr int kRankDirect = 256;   // boundary values ranked by direct comparison
 
@@ -407,7 +408,7 @@ CSA2_DEV int value_bucket(float v, float lo, float scale) {
 
 struct HistSelLds {
   unsigned long long* keys;  // [kTopkCap]
-  int* chosen;               // [>= k]
+  uint32_t* bitmap;          // [M * kSelThreads / 32]
   uint32_t* rhist;           // [512] radix histograms
   unsigned long long* bcast; // [8]
   int* wsum;                 // [kSelThreads / 64]
@@ -415,10 +416,10 @@ struct HistSelLds {
   int* misc;                 // [32]
 };
 
-// Value u of thread t is element t + u * kSelThreads of the set (present when that
-// is below `total`); ix(u) gives its index.
-template <int M, typename IndexFn>
-CSA2_DEV void hist_select(const float (&v)[M], IndexFn ix, int total, int k,
+// Value u of thread t is element t + u * kSelThreads of the row (present when that
+// is below `total`).
+template <int M>
+CSA2_DEV void hist_select(const float (&v)[M], int total, int k,
                           const float* __restrict__ row, int n, const HistSelLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NW = kSelThreads / 64;
@@ -473,48 +474,49 @@ CSA2_DEV void hist_select(const float (&v)[M], IndexFn ix, int total, int k,
   __syncthreads();
   const int bstar = L.misc[0], need = L.misc[1], nbnd = L.misc[2];
   // ---- 4. values above b* are chosen; b*'s values are chosen too when all of
-  // them are needed, else their keys are staged for ranking
+  // them are needed, else their keys are staged for ranking.  Step u of wave w
+  // covers indices kSelThreads * u + 64 w .. + 63: the wave's ballot of the chosen
+  // ones is that 64-bit stretch of the bitmap, stored whole by one lane
   const bool all_bnd = nbnd == need;
   const unsigned long long below = (1ull << lane) - 1ull;
+  unsigned long long* bm64 = reinterpret_cast<unsigned long long*>(L.bitmap);
 #pragma unroll
   for (int u = 0; u < M; ++u) {
     const int bb = ok(u) ? value_bucket(v[u], lo, scale) : -1;
-    const bool take = bb > bstar || (all_bnd && bb == bstar);
+    const unsigned long long mt = __ballot(bb > bstar || (all_bnd && bb == bstar));
+    if (lane == 0) bm64[u * NW + wave] = mt;
     const bool stage = !all_bnd && bb == bstar;
-    const unsigned long long mt = __ballot(take), ms = __ballot(stage);
-    int bt = 0, bs = 0;
-    if (lane == 0) {
-      if (mt) bt = atomicAdd(&L.misc[3], __popcll(mt));
-      if (ms) bs = atomicAdd(&L.misc[4], __popcll(ms));
+    const unsigned long long ms = __ballot(stage);
+    if (ms) {  // the same for the whole wave; most steps stage nothing
+      int bs = 0;
+      if (lane == 0) bs = atomicAdd(&L.misc[4], __popcll(ms));
+      bs = __builtin_amdgcn_readfirstlane(bs);
+      const int ps = bs + __popcll(ms & below);
+      if (stage && ps < kTopkCap) L.keys[ps] = make_key(v[u], tid + u * kSelThreads);
     }
-    bt = __builtin_amdgcn_readfirstlane(bt);
-    bs = __builtin_amdgcn_readfirstlane(bs);
-    if (take) L.chosen[bt + __popcll(mt & below)] = ix(u);
-    const int ps = bs + __popcll(ms & below);
-    if (stage && ps < kTopkCap) L.keys[ps] = make_key(v[u], ix(u));
   }
   __syncthreads();
   if (all_bnd) return;
-  const int base = k - need;  // chosen slots filled so far
+  auto mark = [&](int i) { atomicOr(&L.bitmap[i >> 5], 1u << (i & 31)); };
   if (nbnd <= kRankDirect) {
     if (tid < nbnd) {
       const unsigned long long key = L.keys[tid];
       int rank = 0;
       for (int j = 0; j < nbnd; ++j) rank += L.keys[j] > key ? 1 : 0;
-      if (rank < need) L.chosen[base + rank] = key_index(key);
+      if (rank < need) mark(key_index(key));
     }
   } else if (nbnd <= kTopkCap) {
     const unsigned long long T = radix_kth_u64(L.keys, nbnd, need, L.rhist, L.bcast);
-    if (tid == 0) L.misc[5] = 0;
-    __syncthreads();
     for (int i = tid; i < nbnd; i += kSelThreads) {
       const unsigned long long key = L.keys[i];
-      if (key >= T) L.chosen[base + atomicAdd(&L.misc[5], 1)] = key_index(key);
+      if (key >= T) mark(key_index(key));
     }
   } else {
     int* sel = reinterpret_cast<int*>(L.keys + 1024);
     radix_select_row(row, n, k, sel, reinterpret_cast<uint32_t*>(L.keys), L.misc);
-    for (int i = tid; i < k; i += kSelThreads) L.chosen[i] = sel[i];
+    for (int w = tid; w < M * kSelThreads / 32; w += kSelThreads) L.bitmap[w] = 0u;
+    __syncthreads();
+    for (int i = tid; i < k; i += kSelThreads) mark(sel[i]);
   }
   __syncthreads();
 }
@@ -701,7 +703,7 @@ __global__ __launch_bounds__(kSelThreads, 8) void topk_row_kernel(
   __shared__ uint32_t hist[512];
   __shared__ unsigned long long bcast[8];
   __shared__ int misc[32];
-  __shared__ uint32_t bitmap[kRowCap / 32];
+  __shared__ __attribute__((aligned(8))) uint32_t bitmap[kRowCap / 32];
   __shared__ int wsum[kSelThreads / 64];
   __shared__ float red[2 * kSelThreads / 64];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -718,16 +720,15 @@ __global__ __launch_bounds__(kSelThreads, 8) void topk_row_kernel(
     const int i = tid + u * kSelThreads;
     rv[u] = i < n ? row[i] : 0.0f;
   }
+  // the chosen indices (all < kRowCap) as a bitmap; for the output in ascending
+  // index order, word w's set bits go to slots from the number of bits in words < w
   if (k > 0) {
-    const HistSelLds L{keys, chosen, hist, bcast, wsum, red, misc};
-    hist_select<kPer>(rv, [&](int u) { return tid + u * kSelThreads; }, n, k, row, n, L);
+    const HistSelLds L{keys, bitmap, hist, bcast, wsum, red, misc};
+    hist_select<kPer>(rv, n, k, row, n, L);
+  } else {
+    for (int w2 = tid; w2 < kRowCap / 32; w2 += kSelThreads) bitmap[w2] = 0u;
+    __syncthreads();
   }
-  // output in ascending index order: mark the chosen indices (all < kRowCap) in a
-  // bitmap; word w's set bits go to slots from the number of bits in words < w
-  for (int w2 = tid; w2 < kRowCap / 32; w2 += kSelThreads) bitmap[w2] = 0u;
-  __syncthreads();
-  for (int i = tid; i < k; i += kSelThreads) atomicOr(&bitmap[chosen[i] >> 5], 1u << (chosen[i] & 31));
-  __syncthreads();
   constexpr int kWords = kRowCap / 32;  // one word per thread (kWords <= kSelThreads)
   const uint32_t word = tid < kWords ? bitmap[tid] : 0u;
   const int cnt = __popc(word);
@@ -741,8 +742,8 @@ __global__ __launch_bounds__(kSelThreads, 8) void topk_row_kernel(
   __syncthreads();
   int slot = x - cnt;
   for (int w2 = 0; w2 < wave; ++w2) slot += wsum[w2];
-  // the chosen indices in ascending order, in LDS (chosen[] was last read before
-  // the bitmap barrier), then one parallel pass maps them through the candidate
+  // the chosen indices in ascending order, in LDS, then one parallel pass maps
+  // them through the candidate
   // map and stores them: one memory round trip, not one per chosen index
   for (uint32_t m = word; m; m &= m - 1u) chosen[slot++] = 32 * tid + __ffs(m) - 1;
   __syncthreads();
