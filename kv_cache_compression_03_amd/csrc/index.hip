@@ -175,7 +175,7 @@ constexpr int scan_occupancy(int HI, int QG, bool TM) {
 // and the first batch's key loads go out before the staging barrier.
 // TM: also write the maximum of every 32-entry span of each score row.
 template <int HI, int DI, int QG, bool TM>
-__global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void index_scores_mq_kernel(
+__global__ __launch_bounds__(kScanWaves * 64, 4) void index_scores_mq_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, const int* __restrict__ gather,
     const int* __restrict__ gather_len, const int* __restrict__ q_pos, int m, int Tq, int N, int L,
@@ -268,31 +268,29 @@ __global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void i
   const uint16_t* kb = k_idx + (size_t)b * N * DI;
   const int* gb = gather ? gather + (size_t)b * L : nullptr;
 
-  for (int tile = 0; tile < tiles_per_wave; tile += kScanBatch) {
+  // the keys of a batch (two 16-entry tiles): dead entries read row 0 (their
+  // scores are masked), so every path issues the same loads
+  struct KeyBatch {
     uint4 kv[kScanBatch][KS];
-    int ent[kScanBatch];
-    bool ent_ok[kScanBatch];
+    bool ok[kScanBatch];
+  };
+  auto load_batch = [&](int tile, KeyBatch& kt) {
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) {
       const long long e = wave_first + (long long)(tile + u) * 16 + col;
-      ent[u] = (int)e;
       bool live = (tile + u) < tiles_per_wave && e < Lb;
       long long row = e;
       if (gb) {  // uniform: the gathered row of every slot is read, masked after
         row = gb[min(e, (long long)L - 1)];
         live = live && row >= 0 && row < N;  // an entry outside the cache scores -inf
       }
-      ent_ok[u] = live;
-      // dead entries read row 0 (their scores are masked): the same loads on every path
+      kt.ok[u] = live;
       const uint4* kr = reinterpret_cast<const uint4*>(kb + (size_t)(live ? row : 0) * DI);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kv[u][s] = kr[s * 4 + g];
+      for (int s = 0; s < KS; ++s) kt.kv[u][s] = kr[s * 4 + g];
     }
-    // the staged queries are complete once every wave has passed here; the first
-    // batch's key loads are already in flight (the trip count is the same for all)
-    if constexpr (QL) {
-      if (tile == 0) __syncthreads();
-    }
+  };
+  auto score_batch = [&](int tile, const KeyBatch& kt) {
     // TM: the maximum of the batch's 32 entries for each query row goes out per
     // query tile (the 16 columns of a query are one 16-lane row of the wave)
     const int nmt = (L + kTmaxSpan - 1) / kTmaxSpan;
@@ -311,7 +309,7 @@ __global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void i
       for (int s = 0; s < KS; ++s) {
         const bf16x8_t a = QL ? as_bf16x8(s_qa[(qg * KS + s) * 64 + qli]) : qa[0][s];
 #pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) acc[u] = mfma16x16x32(a, as_bf16x8(kv[u][s]), acc[u]);
+        for (int u = 0; u < kScanBatch; ++u) acc[u] = mfma16x16x32(a, as_bf16x8(kt.kv[u][s]), acc[u]);
       }
       const float4 wq = QL ? s_w[qg * 64 + qli] : wr[0];
       const float wv[4] = {wq.x, wq.y, wq.z, wq.w};
@@ -319,13 +317,13 @@ __global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void i
 #pragma unroll
       for (int u = 0; u < kScanBatch; ++u) {
         if (tile + u >= tiles_per_wave) break;
-        const int e = ent[u];
+        const int e = (int)(wave_first + (long long)(tile + u) * 16 + col);
         float v = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaf(wv[i], fmaxf(acc[u][i], 0.0f), v);
         if (HI >= 8) v += __shfl_xor(v, 16);
         if (HI >= 16) v += __shfl_xor(v, 32);
-        const float sv = (ent_ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
+        const float sv = (kt.ok[u] && e < nvis_row[qg]) ? v : -INFINITY;
         if (writer[qg] && e < L) __builtin_nontemporal_store(sv, &srow0[(size_t)qg * QPT * L + e]);
         if constexpr (TM) bm = fmaxf(bm, e < L ? sv : -INFINITY);
       }
@@ -341,6 +339,20 @@ __global__ __launch_bounds__(kScanWaves * 64, scan_occupancy(HI, QG, TM)) void i
         }
       }
     }
+  };
+  // two batches in registers: the next one's keys are in flight while the current
+  // one is scored (the trip count is the same for every wave)
+  KeyBatch b0, b1;
+  load_batch(0, b0);
+  // the staged queries are complete once every wave has passed here; the first
+  // batch's key loads are already in flight
+  if constexpr (QL) __syncthreads();
+  for (int tile = 0; tile < tiles_per_wave; tile += 2 * kScanBatch) {
+    const bool has1 = tile + kScanBatch < tiles_per_wave;
+    if (has1) load_batch(tile + kScanBatch, b1);
+    score_batch(tile, b0);
+    if (tile + 2 * kScanBatch < tiles_per_wave) load_batch(tile + 2 * kScanBatch, b0);
+    if (has1) score_batch(tile + kScanBatch, b1);
   }
 }
 
@@ -518,7 +530,10 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
   const int qgroups = (qtiles + qg - 1) / qg;
   const long long tiles = ((long long)L + 15) / 16;
   // aim for about CSA2_SCAN_TARGET_WGS workgroups, at most 32 tiles (512 entries) per wave
-  const long long target = CSA2_SCAN_TARGET_WGS;
+#ifndef CSA2_MQ_TARGET_DIV
+#define CSA2_MQ_TARGET_DIV 4
+#endif
+  const long long target = qg >= 2 ? CSA2_SCAN_TARGET_WGS / CSA2_MQ_TARGET_DIV : CSA2_SCAN_TARGET_WGS;
   long long per_wave = ((long long)tiles * B * qgroups + target * kScanWaves - 1) / (target * kScanWaves);
   int tpw = (int)(per_wave < 1 ? 1 : (per_wave > 32 ? 32 : per_wave));
   tpw = (tpw + kScanBatch - 1) / kScanBatch * kScanBatch;
