@@ -131,11 +131,17 @@ def test_prefill_scores(B, Tq, N, h_i, d_i, m, pos):
                                         (64, 12288, 512, "gauss"), (5, 16384, 2048, "gauss"),
                                         (3, 16384, 512, "ties"), (4, 9000, 1, "gauss"),
                                         (2, 10000, 700, "gauss"), (2, 9000, 1500, "gauss"),
-                                        (4, 40000, 512, "short")])
+                                        (4, 40000, 512, "short"), (2, 16384, 512, "flat"),
+                                        (3, 12000, 2048, "flat")])
 def test_topk_paths(R, N, K, kind):
     rng = np.random.default_rng(N + K)
     if kind == "ties":
         s = rng.integers(0, 7, (R, N)).astype(np.float32)   # heavy ties -> exact fallback
+    elif kind == "flat":  # a few larger values over one repeated value: the boundary
+        # bucket holds more values than the key radix select takes -> whole-row select
+        s = np.full((R, N), 0.25, np.float32)
+        for r in range(R):
+            s[r, rng.choice(N, 100, replace=False)] = rng.random(100).astype(np.float32) + 1.0
     else:
         s = rng.standard_normal((R, N)).astype(np.float32)
     vl = rng.integers(N // 2, N + 1, R).astype(np.int32)
