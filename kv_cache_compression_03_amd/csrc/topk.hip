@@ -1162,15 +1162,15 @@ __global__ __launch_bounds__(kPlanThreads) void select_plan_kernel(
   __shared__ uint32_t hist[512];
   __shared__ uint32_t bc[16];
   __shared__ int wsum[kPlanThreads / 64];
-  __shared__ uint32_t bitmap[kBlkWords];
+  __shared__ __attribute__((aligned(8))) uint32_t bitmap[2 * kBlkWords];  // above V, equal to V
   const int r = blockIdx.x, tid = threadIdx.x;
   const int ns_cap = (L + kTmaxSpan - 1) / kTmaxSpan;
   const int n = visible(q_pos, m, r, L);
   const int ns = (n + kTmaxSpan - 1) / kTmaxSpan, nblk = (n + 127) / 128;
   const float* trow = tmax + (size_t)r * ns_cap;
   uint32_t gk[NG], bk[F];  // keys of threshold groups and pool blocks; 0 = empty
+  float4 v[F];             // the span maxima, held for the candidate pass
   {
-    float4 v[F];
     plan_load<F>(trow, ns, v);
     float sm[4 * F];  // span maxima, local span l = 4j + c
 #pragma unroll
@@ -1207,11 +1207,9 @@ __global__ __launch_bounds__(kPlanThreads) void select_plan_kernel(
     block_kth2_u32<NG, F>(gk, bk, kk, ps, T, hist, bc);
   }
   const uint32_t thr = T[0], V = T[1];
-  // ---- candidate spans (maximum >= T): the span maxima again, from L2
+  // ---- candidate spans (maximum >= T), from the span maxima still in registers
   unsigned long long cmask = 0ull;  // bit 4j + c: span 4(j*1024 + t) + c is a candidate
   if (K > 0) {
-    float4 v[F];
-    plan_load<F>(trow, ns, v);
 #pragma unroll
     for (int j = 0; j < F; ++j) {
       const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -1237,45 +1235,37 @@ __global__ __launch_bounds__(kPlanThreads) void select_plan_kernel(
     pw.nct[r] = K > 0 ? tot1 : 0;
     pw.npb[r] = take;
   }
-  // ---- pool blocks: above V all, equal to V in block order until `take`; the
-  // equal blocks are ranked through a bitmap of block indices and the chosen
-  // blocks written ascending through a second one
+  // ---- pool blocks: above V all, equal to V in block order until `take`.  Block
+  // j * kPlanThreads + t sits in thread t, so for each j the 64 lanes of a wave
+  // hold 64 consecutive blocks: the wave's ballots are 64-bit stretches of the
+  // bitmaps of blocks above V and equal to V, stored whole by one lane.  One block
+  // scan of both counts per 32-block word (equal low, above high; each below
+  // 2^16) then gives every word its first output slot.
   if (take > 0) {
-    for (int w2 = tid; w2 < kBlkWords; w2 += kPlanThreads) bitmap[w2] = 0u;
-    __syncthreads();
-    int ngt = 0;
+    const int lane = tid & 63, wave = tid >> 6;
+    unsigned long long* gt64 = reinterpret_cast<unsigned long long*>(bitmap);
+    unsigned long long* eq64 = reinterpret_cast<unsigned long long*>(bitmap + kBlkWords);
 #pragma unroll
     for (int j = 0; j < F; ++j) {
-      const int blk = j * kPlanThreads + tid;
-      if (bk[j] != 0u && bk[j] > V) ++ngt;
-      if (bk[j] != 0u && bk[j] == V) atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
-    }
-    int tgt;
-    block_scan_incl(ngt, wsum, &tgt);  // (its barriers also publish the bitmap)
-    const int need_eq = take - tgt;
-    const uint32_t word = tid < kBlkWords ? bitmap[tid] : 0u;
-    int wtot;
-    const int wbefore = block_scan_incl(__popc(word), wsum, &wtot) - __popc(word);
-    uint32_t keep = 0u;  // the first need_eq equal blocks
-    {
-      int rank = wbefore;
-      for (uint32_t mm = word; mm; mm &= mm - 1u) {
-        const int b = __ffs(mm) - 1;
-        if (rank++ < need_eq) keep |= 1u << b;
+      const unsigned long long mg = __ballot(bk[j] != 0u && bk[j] > V);
+      const unsigned long long me = __ballot(bk[j] != 0u && bk[j] == V);
+      if (lane == 0) {
+        gt64[j * (kPlanThreads / 64) + wave] = mg;
+        eq64[j * (kPlanThreads / 64) + wave] = me;
       }
     }
     __syncthreads();
-    if (tid < kBlkWords) bitmap[tid] = keep;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < F; ++j) {
-      const int blk = j * kPlanThreads + tid;
-      if (bk[j] != 0u && bk[j] > V) atomicOr(&bitmap[blk >> 5], 1u << (blk & 31));
-    }
-    __syncthreads();
-    const uint32_t chosen = tid < kBlkWords ? bitmap[tid] : 0u;
+    const uint32_t gw = tid < kBlkWords ? bitmap[tid] : 0u;
+    const uint32_t ew = tid < kBlkWords ? bitmap[kBlkWords + tid] : 0u;
+    const int packed = __popc(ew) | (__popc(gw) << 16);
     int ptot;
-    int p = block_scan_incl(__popc(chosen), wsum, &ptot) - __popc(chosen);
+    const int before = block_scan_incl(packed, wsum, &ptot) - packed;
+    const int need_eq = max(take - (ptot >> 16), 0);  // equal blocks still to take
+    const int eq_before = before & 0xFFFF;
+    uint32_t chosen = gw;
+    int erank = eq_before;
+    for (uint32_t mm = ew; mm && erank < need_eq; mm &= mm - 1u, ++erank) chosen |= mm & (0u - mm);
+    int p = (before >> 16) + min(eq_before, need_eq);
     for (uint32_t mm = chosen; mm; mm &= mm - 1u) pw.selblk[(size_t)r * PB + p++] = 32 * tid + __ffs(mm) - 1;
   }
 }
