@@ -170,9 +170,11 @@ constexpr int scan_occupancy(int HI, int QG, bool TM) {
 // drafted positions): each key tile is loaded once and multiplied by all of them.
 // The A operands (and head weights) are the same for every wave of the workgroup,
 // so they are staged once in LDS instead of each wave holding QG tiles of them in
-// registers: more waves fit per SIMD, so more key loads are in flight.  All loads
-// are issued from clamped addresses and masked after (no load behind a branch),
-// and the first batch's key loads go out before the staging barrier.
+// registers.  Each wave keeps two key batches in registers (four waves per SIMD):
+// the next batch's keys are in flight while the current one is scored.  Key loads
+// are issued from clamped addresses and masked after (the only branches around
+// them are uniform: whether a wave has a next batch), and the first batch's key
+// loads go out before the staging barrier.
 // TM: also write the maximum of every 32-entry span of each score row.
 template <int HI, int DI, int QG, bool TM>
 __global__ __launch_bounds__(kScanWaves * 64, 4) void index_scores_mq_kernel(
