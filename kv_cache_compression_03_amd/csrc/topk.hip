@@ -1017,7 +1017,8 @@ CSA2_DEV int block_scan_incl(int v, int* wsum, int* total) {
 // highest bit where the non-empty keys differ.  Selection s stops after
 // passes[s] digits (T = the k-th largest key with its lower bits cleared: a lower
 // bound) or when its digit's bucket is taken whole; with 4 passes T is exact.
-// k[s] = 0 skips selection s (T = 0).  hist: 512 uint32 of LDS; bc: 16 uint32.
+// k[s] = 0 skips selection s (T = 0).  hist: 1024 uint32 of LDS (two halves used in
+// turn); bc: 16 uint32.
 template <int NA, int NB>
 CSA2_DEV void block_kth2_u32(const uint32_t (&ka)[NA], const uint32_t (&kb)[NB], const int (&k)[2],
                              const int (&passes)[2], uint32_t (&T)[2], uint32_t* hist, uint32_t* bc) {
@@ -1037,6 +1038,7 @@ CSA2_DEV void block_kth2_u32(const uint32_t (&ka)[NA], const uint32_t (&kb)[NB],
     bc[2 * tid] = 0u;
     bc[2 * tid + 1] = ~0u;
   }
+  if (tid < 512) hist[tid] = 0u;  // the first pass's half of the histogram
   __syncthreads();
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
@@ -1067,23 +1069,26 @@ CSA2_DEV void block_kth2_u32(const uint32_t (&ka)[NA], const uint32_t (&kb)[NB],
     int sh[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) sh[s2] = shift[s2] < 0 ? 0 : shift[s2];
-    if (tid < 512) hist[tid] = 0u;
-    __syncthreads();
+    // two halves of hist alternate: pass p counts into half p mod 2 and clears the
+    // other for pass p + 1 (its last reader, the scan of pass p - 1, finished
+    // before that pass's second barrier)
+    uint32_t* hc = hist + 512 * (pass & 1);
+    if (tid < 512) hist[512 * ((pass + 1) & 1) + tid] = 0u;
     if (live[0]) {
 #pragma unroll
       for (int i = 0; i < NA; ++i)
-        if ((ka[i] & mask[0]) == prefix[0]) atomicAdd(&hist[(ka[i] >> sh[0]) & 255u], 1u);
+        if ((ka[i] & mask[0]) == prefix[0]) atomicAdd(&hc[(ka[i] >> sh[0]) & 255u], 1u);
     }
     if (live[1]) {
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        if ((kb[i] & mask[1]) == prefix[1]) atomicAdd(&hist[256 + ((kb[i] >> sh[1]) & 255u)], 1u);
+        if ((kb[i] & mask[1]) == prefix[1]) atomicAdd(&hc[256 + ((kb[i] >> sh[1]) & 255u)], 1u);
     }
     __syncthreads();
     if (tid < 128) {  // wave s2 finds selection s2's bucket
       const int s2 = tid >> 6;
       if (live[s2]) {
-        const uint32_t* h = hist + 256 * s2;
+        const uint32_t* h = hc + 256 * s2;
         uint32_t hv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) hv[q] = h[4 * lane + q];
@@ -1126,7 +1131,8 @@ CSA2_DEV void block_kth2_u32(const uint32_t (&ka)[NA], const uint32_t (&kb)[NB],
       if (bucket == need[s2] || sh[s2] == 0 || pass + 1 >= passes[s2]) live[s2] = false;
       shift[s2] -= 8;
     }
-    __syncthreads();
+    // no barrier here: the next pass writes bc only after its first barrier, which
+    // every thread reaches after reading bc above
   }
 }
 
@@ -1159,7 +1165,7 @@ __global__ __launch_bounds__(kPlanThreads) void select_plan_kernel(
   constexpr int GSP = 4 * F / NG;                      // spans per group
   constexpr int kBlkWords = kPlanThreads * F / 32;     // bitmap words of all blocks
   static_assert(kBlkWords <= kPlanThreads && GSP >= 1, "plan shape");
-  __shared__ uint32_t hist[512];
+  __shared__ uint32_t hist[1024];  // two alternating 512-bucket halves
   __shared__ uint32_t bc[16];
   __shared__ int wsum[kPlanThreads / 64];
   __shared__ __attribute__((aligned(8))) uint32_t bitmap[2 * kBlkWords];  // above V, equal to V
